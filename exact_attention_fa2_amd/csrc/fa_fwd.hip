@@ -1,0 +1,54 @@
+// Forward kernel instantiations and variant selection.
+#include <hip/hip_runtime.h>
+
+#include "fa.h"
+#include "fa_fwd_kernel.h"
+#include "fa_launch.h"
+
+namespace fa {
+namespace {
+
+template <int D, int DT, bool CAUSAL, int NW, int QB, int BC>
+int launch_one(FwdArgs a, hipStream_t st) {
+  constexpr int BR = NW * 32 * QB;
+  a.nqb = (a.N + BR - 1) / BR;
+  const int64_t total = (int64_t)a.B * a.H * a.nqb;
+  if (total > (INT64_C(1) << 30)) return FA_ERR_DIM;
+  a.total = (int)total;
+  const int grid = (a.total + 7) / 8 * 8;  // a multiple of the 8 XCDs
+  (void)hipGetLastError();
+  hipLaunchKernelGGL((fa_fwd_kernel<D, DT, CAUSAL, NW, QB, BC>), dim3(grid), dim3(NW * 64), 0, st, a);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+template <int D, int DT, bool CAUSAL>
+int pick(FwdArgs a, hipStream_t st) {
+  if constexpr (D == 256)
+    return launch_one<D, DT, CAUSAL, 4, 1, 32>(a, st);
+  else
+    return launch_one<D, DT, CAUSAL, 4, 1, 64>(a, st);
+}
+
+template <int D, int DT>
+int pick_causal(FwdArgs a, bool causal, hipStream_t st) {
+  return causal ? pick<D, DT, true>(a, st) : pick<D, DT, false>(a, st);
+}
+
+template <int DT>
+int pick_d(FwdArgs a, int d, bool causal, hipStream_t st) {
+  switch (d) {
+    case 64: return pick_causal<64, DT>(a, causal, st);
+    case 96: return pick_causal<96, DT>(a, causal, st);
+    case 128: return pick_causal<128, DT>(a, causal, st);
+    case 256: return pick_causal<256, DT>(a, causal, st);
+    default: return FA_ERR_UNSUPPORTED;
+  }
+}
+
+}  // namespace
+
+int launch_fwd(FwdArgs a, int d, int dtype, bool causal, hipStream_t st) {
+  return dtype == FA_BF16 ? pick_d<DT_BF16>(a, d, causal, st) : pick_d<DT_F16>(a, d, causal, st);
+}
+
+}  // namespace fa

@@ -1,0 +1,305 @@
+// FlashAttention-2-style exact attention forward for gfx950.
+//
+// What it computes: O = softmax(scale * Q Kᵀ) V and LSE per row, with the
+// optional causal mask ("FlashAttention explainer" (aitangshan.cn) sections
+// 1 and 7.1). How: one workgroup owns a block of BR query rows (the outer
+// loop over Q blocks of section 5.2); it streams K/V tiles of BC rows
+// through LDS (tiling, section 4.2) and keeps the running row max m and sum l
+// of the online softmax in registers, rescaling the partial output whenever
+// the max moves (section 4.3; "YOLO11 attention swapped for a
+// FlashAttention-2-style implementation" (discosf.com) section 2.2). Only O
+// and LSE are written, once ("FlashAttention explainer" section 5.2).
+//
+// MI355X mapping (our design, not the pages'):
+//  * Each wave owns QW = 32*QB query rows and computes the TRANSPOSED score
+//    tile Sᵀ = K Qᵀ with v_mfma_f32_32x32x16: the query index then sits in
+//    the lane (lane % 32) and the keys in the accumulator registers, so the
+//    row max / row sum are in-register reductions plus one exchange with
+//    lane ^ 32, and the same layout feeds Oᵀ = Vᵀ Pᵀ as its B operand with
+//    no data movement. Oᵀ keeps the query in the lane too, so the rescale by
+//    exp2(m_old - m_new) is a per-lane scalar.
+//  * Vᵀ (the A operand of Oᵀ += Vᵀ Pᵀ) is read from the row-major V tile
+//    with ds_read_b64_tr_b16, the gfx950 LDS transpose read.
+//  * Softmax runs in the log2 domain: c = |scale|*log2(e), p = exp2(s*c - m).
+//    A negative scale is folded into Q by flipping its sign bits (exact).
+//  * The running max is only raised when it grows by more than kRescaleGap
+//    (log2 units): partial sums then stay below 2^kRescaleGap and the costly
+//    rescale of the output accumulator is skipped on most tiles. The final
+//    O = acc / l and LSE = (m + log2 l) ln 2 are exact for any stale m.
+//  * K/V for tile t+1 are fetched into registers while tile t is computed
+//    from the other half of a double-buffered LDS, one barrier per tile.
+//  * Workgroup ids are remapped so that each XCD (workgroups are dealt
+//    round-robin over the 8 XCDs) walks whole heads, sharing K/V in its L2;
+//    causal blocks run longest first.
+#pragma once
+#include "fa_device.h"
+
+namespace fa {
+
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int64_t q_sb, q_sh, q_sr;  // element strides (batch, head, row)
+  int64_t k_sb, k_sh, k_sr;
+  int64_t v_sb, v_sh, v_sr;
+  int64_t o_sb, o_sh, o_sr;
+  int64_t lse_sb, lse_sh;    // lse index = b*lse_sb + h*lse_sh + (row offset) + i
+  const int32_t* cu_seqlens; // null: every sequence has N rows
+  int B, H, N;               // N: rows per sequence (an upper bound with cu_seqlens)
+  int nqb;                   // query blocks per (batch, head)
+  int total;                 // B * H * nqb
+  float c;                   // |scale| * log2(e)
+  uint32_t qsign;            // 0x80008000 when scale < 0, else 0
+};
+
+constexpr float kRescaleGap = 8.0f;
+
+template <int D, int BC>
+struct FwdSmem {
+  static constexpr int KSTR = D + 8;   // padded K row (halves): conflict-free 16-byte reads
+  static constexpr int VSTR = D + 16;  // padded V row (halves): conflict-free transpose reads
+  static constexpr int KTILE = BC * KSTR;
+  static constexpr int VTILE = BC * VSTR;
+  static constexpr int STAGE = KTILE + VTILE;
+  static constexpr int BYTES = 2 * STAGE * 2;
+};
+
+template <int D, int DT, bool CAUSAL, int NW, int QB, int BC>
+__global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
+  constexpr int NT = NW * 64;
+  constexpr int QW = 32 * QB;          // query rows per wave
+  constexpr int BR = NW * QW;          // query rows per workgroup
+  constexpr int KK = D / 16;           // k-steps of Sᵀ = K Qᵀ
+  constexpr int DB = D / 32;           // 32-row blocks of Oᵀ
+  constexpr int KB = BC / 32;          // 32-key blocks of Sᵀ per tile
+  constexpr int CH = BC * D / 8 / NT;  // 16-byte chunks per thread per tensor per tile
+  static_assert(BC * D / 8 % NT == 0, "tile must split evenly over threads");
+  using SM = FwdSmem<D, BC>;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SM::STAGE];
+
+  // ---- workgroup -> (batch, head, query block), XCD-aware ----
+  const int per = gridDim.x >> 3;
+  const int bid = blockIdx.x;
+  const int lid = (bid & 7) * per + (bid >> 3);
+  if (lid >= a.total) return;
+  const int bh = lid / a.nqb;
+  const int qi = lid - bh * a.nqb;
+  const int qblk = CAUSAL ? (a.nqb - 1 - qi) : qi;
+  const int b = bh / a.H, h = bh - b * a.H;
+
+  int64_t row0 = 0;
+  int Nb = a.N;
+  if (a.cu_seqlens) {
+    row0 = a.cu_seqlens[b];
+    Nb = a.cu_seqlens[b + 1] - (int)row0;
+  }
+  if (qblk * BR >= Nb) return;  // uniform over the workgroup
+
+  const uint16_t* Qg = a.q + b * a.q_sb + h * a.q_sh + row0 * a.q_sr;
+  const uint16_t* Kg = a.k + b * a.k_sb + h * a.k_sh + row0 * a.k_sr;
+  const uint16_t* Vg = a.v + b * a.v_sb + h * a.v_sh + row0 * a.v_sr;
+  uint16_t* Og = a.o + b * a.o_sb + h * a.o_sh + row0 * a.o_sr;
+  float* Lg = a.lse + b * a.lse_sb + h * a.lse_sh + row0;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int qw0 = qblk * BR + w * QW;  // first query row of this wave
+
+  // ---- Q fragments (B operand of Sᵀ = K Qᵀ), kept in registers ----
+  u32x4 qf[QB][KK];
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    const int r = qw0 + 32 * j + l32;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (r < Nb) x = *(const u32x4*)(Qg + r * a.q_sr + 16 * kk + 8 * hh);
+      qf[j][kk] = x ^ a.qsign;
+    }
+  }
+
+  const int kv_end = CAUSAL ? min(Nb, (qblk + 1) * BR) : Nb;
+  const int ntiles = (kv_end + BC - 1) / BC;
+
+  // ---- global -> register staging of one K/V tile ----
+  u32x4 kst[CH], vst[CH];
+  auto fetch = [&](int t) {
+    const int base = t * BC;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int ci = tid + NT * c;
+      const int r = ci / (D / 8), col = (ci % (D / 8)) * 8;
+      const int gr = base + r;
+      u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
+      if (gr < kv_end) {
+        xk = *(const u32x4*)(Kg + gr * a.k_sr + col);
+        xv = *(const u32x4*)(Vg + gr * a.v_sr + col);
+      }
+      kst[c] = xk;
+      vst[c] = xv;
+    }
+  };
+  auto stash = [&](int buf) {
+    uint16_t* sk = smem + buf * SM::STAGE;
+    uint16_t* sv = sk + SM::KTILE;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int ci = tid + NT * c;
+      const int r = ci / (D / 8), col = (ci % (D / 8)) * 8;
+      *(u32x4*)(sk + r * SM::KSTR + col) = kst[c];
+      *(u32x4*)(sv + r * SM::VSTR + col) = vst[c];
+    }
+  };
+
+  // ---- running state ----
+  f32x16 oacc[QB][DB];
+#pragma unroll
+  for (int j = 0; j < QB; ++j)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[j][db][r] = 0.f;
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int j = 0; j < QB; ++j) { m_run[j] = -INFINITY; l_run[j] = 0.f; }
+
+  fetch(0);
+  stash(0);
+
+  for (int t = 0; t < ntiles; ++t) {
+    __syncthreads();
+    if (t + 1 < ntiles) fetch(t + 1);
+    const int key0 = t * BC;
+    // causal: skip tiles that lie wholly above this wave's rows
+    const bool active = qw0 < Nb && (!CAUSAL || key0 <= qw0 + QW - 1);
+    if (active) {
+      const uint16_t* sk = smem + (t & 1) * SM::STAGE;
+      const uint16_t* sv = sk + SM::KTILE;
+
+      // Sᵀ = K_t Qᵀ : s[kb][j] covers keys kb*32.. and queries 32j..
+      f32x16 s[KB][QB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int j = 0; j < QB; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[kb][j][r] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const u32x4 ka = *(const u32x4*)(sk + (kb * 32 + l32) * SM::KSTR + 16 * kk + 8 * hh);
+#pragma unroll
+          for (int j = 0; j < QB; ++j) s[kb][j] = mfma32x32x16<DT>(ka, qf[j][kk], s[kb][j]);
+        }
+      }
+
+      // masks: ragged last tile and (causal) keys after the query
+      const bool need_mask = (key0 + BC > Nb) || (CAUSAL && key0 + BC - 1 > qw0);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int j = 0; j < QB; ++j) {
+            const int qrow = qw0 + 32 * j + l32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+              const bool dead = key >= Nb || (CAUSAL && key > qrow);
+              if (dead) s[kb][j][r] = -INFINITY;
+            }
+          }
+      }
+
+      // online softmax (log2 domain)
+      u32x4 pf[QB][BC / 16];
+#pragma unroll
+      for (int j = 0; j < QB; ++j) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][j][r]);
+        mx = fmaxf(mx, xor_lane32(mx));
+        const float m_new = fmaxf(m_run[j], mx * a.c);
+        if (wave_any(m_new > m_run[j] + kRescaleGap)) {
+          const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[j] - m_new);
+          l_run[j] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[j][db][r] *= alpha;
+          m_run[j] = m_new;
+        }
+        const float mref = (m_run[j] == -INFINITY) ? 0.f : m_run[j];
+        float lsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          float p[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float x = __builtin_fmaf(s[kb][j][r], a.c, -mref);
+            // a masked score stays masked even when c == 0 (scale 0)
+            if (need_mask) x = (s[kb][j][r] == -INFINITY) ? -INFINITY : x;
+            p[r] = fast_exp2(x);
+            lsum += p[r];
+          }
+#pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2) {
+            u32x4 x;
+            x[0] = pack2<DT>(p[8 * c2 + 0], p[8 * c2 + 1]);
+            x[1] = pack2<DT>(p[8 * c2 + 2], p[8 * c2 + 3]);
+            x[2] = pack2<DT>(p[8 * c2 + 4], p[8 * c2 + 5]);
+            x[3] = pack2<DT>(p[8 * c2 + 6], p[8 * c2 + 7]);
+            pf[j][2 * kb + c2] = x;
+          }
+        }
+        l_run[j] += lsum;
+      }
+
+      // Oᵀ += Vᵀ Pᵀ ; k-slot 8*hh + 4*rd + e of chunk ci is key 16*ci + 8*rd + 4*hh + e
+      const int g = lane >> 4, s16 = lane & 15;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int ci = 0; ci < BC / 16; ++ci) {
+          const int col = db * 32 + (g & 1) * 16 + 4 * (s16 & 3);
+          const int rowa = 16 * ci + 4 * hh + (s16 >> 2);
+          const u32x2 lo = lds_read_tr4(sv + rowa * SM::VSTR + col);
+          const u32x2 hi = lds_read_tr4(sv + (rowa + 8) * SM::VSTR + col);
+          const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+          for (int j = 0; j < QB; ++j) oacc[j][db] = mfma32x32x16<DT>(va, pf[j][ci], oacc[j][db]);
+        }
+      }
+    }
+    if (t + 1 < ntiles) stash((t + 1) & 1);
+  }
+
+  // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    const float l_tot = l_run[j] + xor_lane32(l_run[j]);
+    const float inv = 1.f / l_tot;
+    const int qrow = qw0 + 32 * j + l32;
+    if (qrow < Nb) {
+      uint16_t* orow = Og + qrow * a.o_sr;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          u32x2 x;
+          x[0] = pack2<DT>(oacc[j][db][4 * g4 + 0] * inv, oacc[j][db][4 * g4 + 1] * inv);
+          x[1] = pack2<DT>(oacc[j][db][4 * g4 + 2] * inv, oacc[j][db][4 * g4 + 3] * inv);
+          *(u32x2*)(orow + db * 32 + 8 * g4 + 4 * hh) = x;
+        }
+      if (hh == 0) Lg[qrow] = (m_run[j] + fast_log2(l_tot)) * kLn2;
+    }
+  }
+}
+
+}  // namespace fa

@@ -1,0 +1,63 @@
+"""Shared helpers for the GPU parity tests: run the HIP path, run the oracle on
+the very same input bits, and apply the tolerance gate.
+
+Gate for O (fp16 / bf16 outputs): |O_gpu - O_ref| <= atol + ulp(O_ref)/2, with
+atol = 2e-3 (fp16) or 1e-2 (bf16) and ulp the spacing of the output dtype at
+|O_ref| (rounding the exact result to the output dtype alone may cost half an
+ulp, which exceeds atol for bf16 once |O| >= 2). LSE: |LSE_gpu - LSE_ref| <= 1e-3.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from exact_attention_fa2_amd import inputs
+
+ATOL = {"f16": 2e-3, "bf16": 1e-2}
+LSE_ATOL = 1e-3
+MANT = {"f16": 10, "bf16": 7}
+EMIN = {"f16": -14, "bf16": -126}
+
+
+def ulp(x: np.ndarray, dtype: str) -> np.ndarray:
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    e = np.maximum(e, EMIN[dtype])
+    return np.exp2(e - MANT[dtype])
+
+
+def gate_o(o_gpu: np.ndarray, o_ref: np.ndarray, dtype: str, what: str = "O") -> float:
+    o_gpu = np.asarray(o_gpu, np.float64)
+    err = np.abs(o_gpu - o_ref)
+    bound = ATOL[dtype] + 0.5 * ulp(o_ref, dtype)
+    bad = ~(err <= bound)
+    if bad.any():
+        i = np.unravel_index(np.argmax(np.where(bad, err - bound, -np.inf)), err.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {err.size} outside the gate; worst at {i}: "
+                             f"gpu={o_gpu[i]!r} ref={o_ref[i]!r} err={err[i]:.3e} bound={bound[i]:.3e}")
+    return float(err.max()) if err.size else 0.0
+
+
+def gate_lse(lse_gpu: np.ndarray, lse_ref: np.ndarray) -> float:
+    err = np.abs(np.asarray(lse_gpu, np.float64) - lse_ref)
+    if err.size and not (err <= LSE_ATOL).all():
+        i = np.unravel_index(np.argmax(np.nan_to_num(err, nan=np.inf)), err.shape)
+        raise AssertionError(f"LSE: max err {err[i]:.3e} at {i}: gpu={lse_gpu[i]} ref={lse_ref[i]}")
+    return float(err.max()) if err.size else 0.0
+
+
+def to64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().to(torch.float64).numpy()
+
+
+def decode(t: torch.Tensor, dtype: str) -> np.ndarray:
+    return oracle.decode(inputs.bits(t.cpu()), dtype)
+
+
+def sample_rows(B: int, H: int, N: int, n: int, seed: int) -> np.ndarray:
+    """(b, h, i) rows: the first and last rows of every head plus n random ones."""
+    rng = np.random.default_rng(seed)
+    rows = [(b, h, i) for b in range(B) for h in range(H) for i in {0, N - 1}]
+    rows += [(int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(N))) for _ in range(n)]
+    return np.unique(np.array(rows, dtype=np.int64), axis=0)

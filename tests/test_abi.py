@@ -1,0 +1,138 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+that include/fa.h declares, and rejects bad arguments on the host before any
+HIP call (so the fake pointers below are never dereferenced or launched on).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_fa2_amd as fa
+from exact_attention_fa2_amd import build as fabuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+OK, NULL, DIM, UNSUP, SCALE, ALIGN, LAUNCH, ALIAS, DEVICE = 0, -1, -2, -3, -4, -5, -6, -7, -8
+A = 0x7F0000000000  # fake, 16-byte aligned device addresses (never touched)
+MB = 1 << 20
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fa.LIB_PATH):
+        fabuild.build()
+    return fa.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_functions()
+    for n in ("fa_fwd", "fa_fwd_strided", "fa_fwd_varlen", "fa_bwd", "fa_bwd_workspace_bytes",
+              "fa_fwd_fa1_order", "fa_fwd_fa1_workspace_bytes", "fa_strerror", "fa_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    raw = ctypes.CDLL(fa.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(raw, n), n
+    assert set(declared_functions()) == set(fa._SIGS), "binding signatures out of sync with fa.h"
+
+
+def test_strerror_and_version(L):
+    for code in (OK, NULL, DIM, UNSUP, SCALE, ALIGN, LAUNCH, ALIAS, DEVICE):
+        s = L.fa_strerror(code).decode()
+        assert s and "unknown" not in s
+    assert "unknown" in L.fa_strerror(12345).decode()
+    assert L.fa_version() >> 16 == 1
+
+
+def fwd(L, q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 256 * MB,
+        B=1, H=2, N=64, d=64, scale=0.125, causal=0, dtype=0):
+    return L.fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, None)
+
+
+def test_fwd_argument_errors(L):
+    assert fwd(L, q=None) == NULL
+    assert fwd(L, lse=None) == NULL
+    assert fwd(L, B=-1) == DIM
+    assert fwd(L, N=-5) == DIM
+    assert fwd(L, d=80) == UNSUP
+    assert fwd(L, d=0, N=4) == UNSUP  # only B, H or N may be zero
+    assert fwd(L, dtype=2) == UNSUP
+    assert fwd(L, scale=float("nan")) == SCALE
+    assert fwd(L, scale=float("inf")) == SCALE
+    assert fwd(L, q=A + 8) == ALIGN
+    assert fwd(L, lse=A + 256 * MB + 2) == ALIGN
+    assert fwd(L, B=1 << 20, H=1 << 20, N=1 << 20, d=64) == DIM  # 2^66 elements
+    assert fwd(L, o=A + 16) == ALIAS          # o overlaps q
+    assert fwd(L, lse=A + 128 * MB + 64) == ALIAS  # lse overlaps v
+
+
+def test_fwd_zero_sizes_are_noops(L):
+    for kw in ({"B": 0}, {"H": 0}, {"N": 0}):
+        assert fwd(L, q=None, k=None, v=None, o=None, lse=None, **kw) == OK
+
+
+def test_fwd_error_precedence(L):
+    # size errors are reported before pointer errors, so a bad call never launches
+    assert fwd(L, q=None, B=-1) == DIM
+    assert fwd(L, q=None, d=48) == UNSUP
+
+
+def strided(L, strides=None, **kw):
+    s = strides or [64 * 8 * 64, 64, 8 * 64] * 4
+    args = dict(q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 256 * MB,
+                B=2, H=8, N=64, d=64, scale=0.125, causal=0, dtype=1)
+    args.update(kw)
+    return L.fa_fwd_strided(args["q"], args["k"], args["v"], args["o"], args["lse"], args["B"], args["H"],
+                            args["N"], args["d"], args["scale"], args["causal"], args["dtype"], *s, None)
+
+
+def test_strided_argument_errors(L):
+    s = [64 * 8 * 64, 64, 8 * 64] * 4
+    bad = list(s)
+    bad[2] = 8 * 64 + 4  # row stride not a multiple of 8 elements
+    assert strided(L, bad) == ALIGN
+    bad = list(s)
+    bad[4] = -64
+    assert strided(L, bad) == DIM
+    bad = list(s)
+    bad[0] = 1 << 62  # far element out of the addressable range
+    assert strided(L, bad) == DIM
+    assert strided(L, o=A) == ALIAS
+    assert strided(L, v=None) == NULL
+    assert strided(L, d=32) == UNSUP
+
+
+def test_varlen_argument_errors(L):
+    def call(**kw):
+        a = dict(q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 256 * MB, cu=A + 300 * MB,
+                 B=3, T=300, maxs=128, H=4, d=64, scale=0.1, causal=1, dtype=0)
+        a.update(kw)
+        return L.fa_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"], a["B"], a["T"], a["maxs"],
+                               a["H"], a["d"], a["scale"], a["causal"], a["dtype"], None)
+    assert call(cu=None) == NULL
+    assert call(maxs=-1) == DIM
+    assert call(maxs=301) == DIM
+    assert call(T=-3) == DIM
+    assert call(B=-1) == DIM
+    assert call(B=0) == OK
+    assert call(cu=A + 300 * MB + 2) == ALIGN
+    assert call(d=40) == UNSUP
+
+
+def test_python_binding_rejects_cpu_tensors(L):
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        fa.attention(q, q, q)
+    with pytest.raises(TypeError):
+        fa._dtype_code(torch.zeros(1, dtype=torch.float32))

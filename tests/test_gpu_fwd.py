@@ -1,0 +1,243 @@
+"""GPU parity of the forward kernels against the fp64 oracle (same input bits).
+
+Runs through the C ABI (``fa_fwd`` / ``fa_fwd_strided`` / ``fa_fwd_varlen``
+via the ctypes binding). Needs an MI355X and the built libfa.so.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity as P
+import exact_attention_fa2_amd as fa
+from exact_attention_fa2_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def run_case(B, H, N, d, dtype, causal, seed, scale=None, sigma_qk=1.0, sigma_v=1.0, rows=None):
+    say(f"[fa_fwd] B{B} H{H} N{N} d{d} {dtype} causal={causal} seed={seed} scale={scale} sqk={sigma_qk}")
+    q, k, v = inputs.make_qkv(B, H, N, d, dtype, seed, sigma_qk, sigma_v)
+    sc = d ** -0.5 if scale is None else scale
+    o, lse = fa.attention(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, scale=sc)
+    torch.cuda.synchronize()
+    og, lg = P.to64(o), P.to64(lse)
+    qd, kd, vd = (P.decode(x, dtype) for x in (q, k, v))
+    if rows is None:
+        ro, rl = oracle.attention_fwd(qd, kd, vd, sc, causal)
+        eo = P.gate_o(og, ro, dtype)
+        el = P.gate_lse(lg, rl)
+    else:
+        ro, rl = oracle.attention_fwd_rows(qd, kd, vd, sc, causal, rows)
+        eo = P.gate_o(og[rows[:, 0], rows[:, 1], rows[:, 2]], ro, dtype)
+        el = P.gate_lse(lg[rows[:, 0], rows[:, 1], rows[:, 2]], rl)
+    assert np.isfinite(og).all() and np.isfinite(lg).all()
+    return eo, el
+
+
+# ---------------------------------------------------------------------------
+# the five workloads
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("name", list(inputs.WORKLOADS))
+def test_workload_parity(name, seed):
+    w = inputs.WORKLOADS[name]
+    rows = None
+    if w.B * w.H * w.N * w.N > 64 * 400 * 400 * 4:  # large: sampled rows, all heads touched
+        rows = P.sample_rows(w.B, w.H, w.N, 384, seed)
+    eo, el = run_case(w.B, w.H, w.N, w.d, w.dtype, w.causal, seed, None, w.sigma_qk, w.sigma_v, rows)
+    say(f"  {name} seed {seed}: max|dO| {eo:.3e}  max|dLSE| {el:.3e}")
+
+
+def test_long_causal_variance3_reading():
+    # the other reading of the large-logit workload: variance 3 (sigma = sqrt 3)
+    w = inputs.WORKLOADS["n8192_causal"]
+    rows = P.sample_rows(w.B, w.H, w.N, 256, 5)
+    run_case(w.B, w.H, w.N, w.d, w.dtype, True, 5, None, math.sqrt(3.0), 1.0, rows)
+
+
+# ---------------------------------------------------------------------------
+# ragged and degenerate shapes, every head dim, both dtypes
+# ---------------------------------------------------------------------------
+EDGE_N = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 257, 400, 401]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", EDGE_N)
+def test_edge_lengths_d64(N, causal, dtype):
+    run_case(2, 3, N, 64, dtype, causal, seed=N)
+
+
+@pytest.mark.parametrize("d", [96, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 17, 64, 129, 300])
+def test_edge_lengths_other_dims(N, d, causal):
+    run_case(1, 3, N, d, "bf16" if d != 96 else "f16", causal, seed=N + d)
+
+
+@pytest.mark.parametrize("N", [1000, 1537])
+def test_multi_block_causal_large_logits(N):
+    run_case(1, 4, N, 128, "bf16", True, seed=11, sigma_qk=3.0)
+    run_case(1, 4, N, 64, "f16", True, seed=12, sigma_qk=3.0)
+
+
+def test_scale_variants():
+    run_case(1, 2, 130, 64, "f16", False, seed=3, scale=0.0)
+    run_case(1, 2, 130, 64, "f16", True, seed=3, scale=0.0)
+    run_case(1, 2, 130, 64, "f16", False, seed=4, scale=-0.2)
+    run_case(1, 2, 130, 128, "bf16", True, seed=4, scale=-0.05)
+    run_case(1, 2, 97, 64, "bf16", False, seed=5, scale=1.0)
+
+
+# ---------------------------------------------------------------------------
+# identities on the GPU
+# ---------------------------------------------------------------------------
+def _gpu(q, k, v, causal, scale):
+    o, lse = fa.attention(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_constant_v_is_returned(dtype, causal):
+    say(f"[identity] constant V {dtype} causal={causal}")
+    q, k, _ = inputs.make_qkv(1, 4, 1000, 128, dtype, 21, sigma_qk=3.0)
+    c = inputs.make_like(torch.empty(128, dtype=q.dtype), 22)
+    v = c.expand(1, 4, 1000, 128).contiguous()
+    o, _ = _gpu(q, k, v, causal, 128 ** -0.5)
+    ref = v.to(torch.float64).numpy()
+    err = np.abs(P.to64(o) - ref)
+    assert (err <= P.ulp(ref, dtype)).all(), err.max()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_q_zero_gives_mean(causal):
+    say(f"[identity] Q=0 causal={causal}")
+    _, k, v = inputs.make_qkv(2, 2, 400, 64, "f16", 31)
+    q = torch.zeros_like(k)
+    o, lse = _gpu(q, k, v, causal, 0.125)
+    vv = v.to(torch.float64).numpy()
+    if causal:
+        mean = np.cumsum(vv, axis=2) / np.arange(1, 401)[None, None, :, None]
+        lse_ref = np.log(np.arange(1, 401))[None, None]
+    else:
+        mean = np.broadcast_to(vv.mean(axis=2, keepdims=True), vv.shape)
+        lse_ref = np.full((1, 1, 400), math.log(400))
+    P.gate_o(P.to64(o), mean, "f16")
+    P.gate_lse(P.to64(lse), np.broadcast_to(lse_ref, (2, 2, 400)))
+
+
+def test_causal_row0_is_exact():
+    say("[identity] causal row 0")
+    q, k, v = inputs.make_qkv(1, 3, 777, 128, "bf16", 41, sigma_qk=3.0)
+    o, lse = _gpu(q, k, v, True, 128 ** -0.5)
+    assert torch.equal(o[:, :, 0], v[:, :, 0])
+    s0 = (q[0, :, 0].double() * k[0, :, 0].double()).sum(-1) * 128 ** -0.5
+    assert np.allclose(lse[0, :, 0].double().numpy(), s0.numpy(), atol=1e-4)
+
+
+def test_dominant_score_selects_row():
+    say("[identity] dominant score")
+    N, d = 300, 64
+    q = torch.zeros(1, 1, N, d)
+    k = torch.randn(1, 1, N, d, generator=torch.Generator().manual_seed(3)) * 0.01
+    q[..., 0] = 1.0
+    k[0, 0, 123] = 0.0
+    k[0, 0, 123, 0] = 30.0 / 0.125
+    v = torch.randn(1, 1, N, d, generator=torch.Generator().manual_seed(4))
+    q, k, v = q.half(), k.half(), v.half()
+    o, _ = _gpu(q, k, v, False, 0.125)
+    ref = np.broadcast_to(v[0, 0, 123].double().numpy(), (N, d))
+    P.gate_o(P.to64(o[0, 0]), ref, "f16")
+
+
+def test_deterministic():
+    q, k, v = (t.to(DEV) for t in inputs.make_qkv(2, 4, 1000, 64, "f16", 51))
+    o1, l1 = fa.attention(q, k, v, causal=True)
+    o2, l2 = fa.attention(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_side_stream():
+    q, k, v = (t.to(DEV) for t in inputs.make_qkv(1, 2, 200, 64, "bf16", 52))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o1, l1 = fa.attention(q, k, v)
+    s.synchronize()
+    o2, l2 = fa.attention(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ---------------------------------------------------------------------------
+# layouts at the boundary: [B, N, H, d] and packed QKV [B, N, 3, H, d]
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+def test_bnhd_and_packed_layouts(causal):
+    say(f"[fa_fwd_strided] causal={causal}")
+    B, N, H, d, dtype = 2, 400, 8, 64, "bf16"
+    q, k, v = inputs.make_qkv(B, N, H, d, dtype, 61)  # drawn directly in [B, N, H, d]
+    o, lse = fa.attention_bnhd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal)
+    torch.cuda.synchronize()
+    perm = lambda t: P.decode(t, dtype).transpose(0, 2, 1, 3)
+    ro, rl = oracle.attention_fwd(perm(q), perm(k), perm(v), d ** -0.5, causal)
+    P.gate_o(P.to64(o).transpose(0, 2, 1, 3), ro, dtype)
+    P.gate_lse(P.to64(lse), rl)
+
+    qkv = torch.stack([q, k, v], dim=2).contiguous()  # [B, N, 3, H, d]
+    o2, lse2 = fa.attention_qkvpacked(qkv.to(DEV), causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.cpu(), o.cpu()) and torch.equal(lse2.cpu(), lse.cpu())
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_packed_qkv_pages_shape(d):
+    # an 80x80 map with C = 256 channels split into heads of d
+    say(f"[fa_fwd_strided] packed qkv N=6400 C=256 d={d}")
+    B, N, H = 1, 6400, 256 // d
+    g = torch.Generator().manual_seed(71)
+    qkv = torch.randn(B, N, 3, H, d, generator=g).half()
+    o, lse = fa.attention_qkvpacked(qkv.to(DEV))
+    torch.cuda.synchronize()
+    rows = P.sample_rows(B, H, N, 128, 71)
+    dd = lambda i: P.decode(qkv[:, :, i].contiguous(), "f16").transpose(0, 2, 1, 3)
+    ro, rl = oracle.attention_fwd_rows(dd(0), dd(1), dd(2), d ** -0.5, False, rows)
+    og = P.to64(o).transpose(0, 2, 1, 3)
+    P.gate_o(og[rows[:, 0], rows[:, 1], rows[:, 2]], ro, "f16")
+    P.gate_lse(P.to64(lse)[rows[:, 0], rows[:, 1], rows[:, 2]], rl)
+
+
+# ---------------------------------------------------------------------------
+# variable-length packed batches
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d,dtype", [(64, "f16"), (128, "bf16")])
+def test_varlen(causal, d, dtype):
+    seqlens = [400, 1, 100, 129, 0, 64, 1600, 37]
+    say(f"[fa_fwd_varlen] {seqlens} d={d} {dtype} causal={causal}")
+    H = 4
+    q, k, v, cu = inputs.make_varlen(seqlens, H, d, dtype, 81)
+    o, lse = fa.attention_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), max(seqlens), causal=causal)
+    torch.cuda.synchronize()
+    og, lg = P.to64(o), P.to64(lse)
+    qd, kd, vd = (P.decode(x, dtype) for x in (q, k, v))
+    for b, n in enumerate(seqlens):
+        s0 = int(cu[b])
+        if n == 0:
+            continue
+        sl = slice(s0, s0 + n)
+        t = lambda x: x[sl].transpose(1, 0, 2)[None]  # [1, H, n, d]
+        ro, rl = oracle.attention_fwd(t(qd), t(kd), t(vd), d ** -0.5, causal)
+        P.gate_o(og[sl].transpose(1, 0, 2)[None], ro, dtype, what=f"O seq {b}")
+        P.gate_lse(lg[:, sl][None], rl)
