@@ -62,8 +62,12 @@ int device_ok() {
   return ok ? FA_OK : FA_ERR_DEVICE;
 }
 
+// The kernels run the softmax in the log2 domain with c = |scale| * log2(e) and
+// fold a negative scale into Q's sign. c is kept >= 1e-30 so that a masked
+// score (-inf) times c stays -inf; for scale 0 every |s * c| is then below
+// 2^-60 and exp2 of it rounds to exactly 1, i.e. uniform weights as required.
 void fill_scale(FwdArgs& a, float scale) {
-  a.c = std::fabs(scale) * kLog2e;
+  a.c = std::fmax(std::fabs(scale) * kLog2e, 1e-30f);
   a.qsign = scale < 0.f ? 0x80008000u : 0u;
 }
 

@@ -51,7 +51,7 @@ struct FwdArgs {
   int B, H, N;               // N: rows per sequence (an upper bound with cu_seqlens)
   int nqb;                   // query blocks per (batch, head)
   int total;                 // B * H * nqb
-  float c;                   // |scale| * log2(e)
+  float c;                   // max(|scale| * log2(e), 1e-30): strictly positive
   uint32_t qsign;            // 0x80008000 when scale < 0, else 0
 };
 
@@ -66,6 +66,111 @@ struct FwdSmem {
   static constexpr int STAGE = KTILE + VTILE;
   static constexpr int BYTES = 2 * STAGE * 2;
 };
+
+// One K/V tile for one wave: Sᵀ = K Qᵀ, online-softmax update, Oᵀ += Vᵀ Pᵀ.
+// Masked tiles (wave-uniform flag) apply the ragged-tail and causal masks.
+template <int D, int DT, bool CAUSAL, int QB, int BC, int KSTR, int VSTR>
+__device__ __forceinline__ void tile_step_fwd(bool masked, const uint16_t* __restrict__ sk,
+                                               const uint16_t* __restrict__ sv, int key0, int Nb,
+                                               int qw0, int lane, float c, const u32x4 (&qf)[QB][D / 16],
+                                               f32x16 (&oacc)[QB][D / 32], float (&m_run)[QB],
+                                               float (&l_run)[QB]) {
+  constexpr int KK = D / 16, DB = D / 32, KB = BC / 32;
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  // Sᵀ = K_t Qᵀ : s[kb][j] covers keys kb*32.. and queries 32j..
+  f32x16 s[KB][QB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int j = 0; j < QB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][j][r] = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const u32x4 ka = *(const u32x4*)(sk + (kb * 32 + l32) * KSTR + 16 * kk + 8 * hh);
+#pragma unroll
+      for (int j = 0; j < QB; ++j) s[kb][j] = mfma32x32x16<DT>(ka, qf[j][kk], s[kb][j]);
+    }
+  }
+
+  if (masked) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < QB; ++j) {
+        const int qrow = qw0 + 32 * j + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const bool dead = key >= Nb || (CAUSAL && key > qrow);
+          if (dead) s[kb][j][r] = -INFINITY;
+        }
+      }
+  }
+
+  // online softmax (log2 domain)
+  u32x4 pf[QB][BC / 16];
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][j][r]);
+    mx = fmaxf(mx, xor_lane32(mx));
+    const float m_new = fmaxf(m_run[j], mx * c);
+    if (wave_any(m_new > m_run[j] + kRescaleGap)) {
+      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[j] - m_new);
+      l_run[j] *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[j][db][r] *= alpha;
+      m_run[j] = m_new;
+    }
+    const float mref = (m_run[j] == -INFINITY) ? 0.f : m_run[j];
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        // c > 0 always (clamped on the host), so a masked -inf stays -inf
+        p[r] = fast_exp2(__builtin_fmaf(s[kb][j][r], c, -mref));
+        lsum += p[r];
+      }
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        u32x4 x;
+        x[0] = pack2<DT>(p[8 * c2 + 0], p[8 * c2 + 1]);
+        x[1] = pack2<DT>(p[8 * c2 + 2], p[8 * c2 + 3]);
+        x[2] = pack2<DT>(p[8 * c2 + 4], p[8 * c2 + 5]);
+        x[3] = pack2<DT>(p[8 * c2 + 6], p[8 * c2 + 7]);
+        pf[j][2 * kb + c2] = x;
+      }
+    }
+    l_run[j] += lsum;
+  }
+
+  // Oᵀ += Vᵀ Pᵀ ; k-slot 8*hh + 4*rd + e of chunk ci is key 16*ci + 8*rd + 4*hh + e
+  const int g = lane >> 4, s16 = lane & 15;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int ci = 0; ci < BC / 16; ++ci) {
+      const int col = db * 32 + (g & 1) * 16 + 4 * (s16 & 3);
+      const int rowa = 16 * ci + 4 * hh + (s16 >> 2);
+      const u32x2 lo = lds_read_tr4(sv + rowa * VSTR + col);
+      const u32x2 hi = lds_read_tr4(sv + (rowa + 8) * VSTR + col);
+      const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+      for (int j = 0; j < QB; ++j) oacc[j][db] = mfma32x32x16<DT>(va, pf[j][ci], oacc[j][db]);
+    }
+  }
+}
 
 template <int D, int DT, bool CAUSAL, int NW, int QB, int BC>
 __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
@@ -170,113 +275,17 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
   fetch(0);
   stash(0);
 
+
   for (int t = 0; t < ntiles; ++t) {
     __syncthreads();
     if (t + 1 < ntiles) fetch(t + 1);
     const int key0 = t * BC;
-    // causal: skip tiles that lie wholly above this wave's rows
-    const bool active = qw0 < Nb && (!CAUSAL || key0 <= qw0 + QW - 1);
-    if (active) {
-      const uint16_t* sk = smem + (t & 1) * SM::STAGE;
-      const uint16_t* sv = sk + SM::KTILE;
-
-      // Sᵀ = K_t Qᵀ : s[kb][j] covers keys kb*32.. and queries 32j..
-      f32x16 s[KB][QB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int j = 0; j < QB; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[kb][j][r] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const u32x4 ka = *(const u32x4*)(sk + (kb * 32 + l32) * SM::KSTR + 16 * kk + 8 * hh);
-#pragma unroll
-          for (int j = 0; j < QB; ++j) s[kb][j] = mfma32x32x16<DT>(ka, qf[j][kk], s[kb][j]);
-        }
-      }
-
-      // masks: ragged last tile and (causal) keys after the query
-      const bool need_mask = (key0 + BC > Nb) || (CAUSAL && key0 + BC - 1 > qw0);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int j = 0; j < QB; ++j) {
-            const int qrow = qw0 + 32 * j + l32;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-              const bool dead = key >= Nb || (CAUSAL && key > qrow);
-              if (dead) s[kb][j][r] = -INFINITY;
-            }
-          }
-      }
-
-      // online softmax (log2 domain)
-      u32x4 pf[QB][BC / 16];
-#pragma unroll
-      for (int j = 0; j < QB; ++j) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][j][r]);
-        mx = fmaxf(mx, xor_lane32(mx));
-        const float m_new = fmaxf(m_run[j], mx * a.c);
-        if (wave_any(m_new > m_run[j] + kRescaleGap)) {
-          const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[j] - m_new);
-          l_run[j] *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[j][db][r] *= alpha;
-          m_run[j] = m_new;
-        }
-        const float mref = (m_run[j] == -INFINITY) ? 0.f : m_run[j];
-        float lsum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          float p[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float x = __builtin_fmaf(s[kb][j][r], a.c, -mref);
-            // a masked score stays masked even when c == 0 (scale 0)
-            if (need_mask) x = (s[kb][j][r] == -INFINITY) ? -INFINITY : x;
-            p[r] = fast_exp2(x);
-            lsum += p[r];
-          }
-#pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2) {
-            u32x4 x;
-            x[0] = pack2<DT>(p[8 * c2 + 0], p[8 * c2 + 1]);
-            x[1] = pack2<DT>(p[8 * c2 + 2], p[8 * c2 + 3]);
-            x[2] = pack2<DT>(p[8 * c2 + 4], p[8 * c2 + 5]);
-            x[3] = pack2<DT>(p[8 * c2 + 6], p[8 * c2 + 7]);
-            pf[j][2 * kb + c2] = x;
-          }
-        }
-        l_run[j] += lsum;
-      }
-
-      // Oᵀ += Vᵀ Pᵀ ; k-slot 8*hh + 4*rd + e of chunk ci is key 16*ci + 8*rd + 4*hh + e
-      const int g = lane >> 4, s16 = lane & 15;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int ci = 0; ci < BC / 16; ++ci) {
-          const int col = db * 32 + (g & 1) * 16 + 4 * (s16 & 3);
-          const int rowa = 16 * ci + 4 * hh + (s16 >> 2);
-          const u32x2 lo = lds_read_tr4(sv + rowa * SM::VSTR + col);
-          const u32x2 hi = lds_read_tr4(sv + (rowa + 8) * SM::VSTR + col);
-          const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-          for (int j = 0; j < QB; ++j) oacc[j][db] = mfma32x32x16<DT>(va, pf[j][ci], oacc[j][db]);
-        }
-      }
-    }
+    const uint16_t* sk = smem + (t & 1) * SM::STAGE;
+    const uint16_t* sv = sk + SM::KTILE;
+    // ragged last tile, or (causal) keys after some query of this wave
+    const bool need_mask = (key0 + BC > Nb) || (CAUSAL && key0 + BC - 1 > qw0);
+    tile_step_fwd<D, DT, CAUSAL, QB, BC, SM::KSTR, SM::VSTR>(need_mask, sk, sv, key0, Nb, qw0, lane,
+                                                             a.c, qf, oacc, m_run, l_run);
     if (t + 1 < ntiles) stash((t + 1) & 1);
   }
 
