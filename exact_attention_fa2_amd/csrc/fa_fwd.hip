@@ -3,6 +3,7 @@
 
 #include "fa.h"
 #include "fa_fwd_kernel.h"
+#include "fa_fwd_pipe.h"
 #include "fa_launch.h"
 
 namespace fa {
@@ -21,10 +22,40 @@ int launch_one(FwdArgs a, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+template <int D, int DT, bool CAUSAL, int NW, int QB, int BC>
+int launch_pipe(FwdArgs a, hipStream_t st) {
+  constexpr int BR = NW * 32 * QB;
+  a.nqb = (a.N + BR - 1) / BR;
+  const int64_t total = (int64_t)a.B * a.H * a.nqb;
+  if (total > (INT64_C(1) << 30)) return FA_ERR_DIM;
+  a.total = (int)total;
+  const int grid = (a.total + 7) / 8 * 8;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL((fa_fwd_pipe_kernel<D, DT, CAUSAL, NW, QB, BC>), dim3(grid), dim3(NW * 64), 0, st,
+                     a);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+// The pipelined kernel addresses K/V rows with 32-bit buffer offsets: every
+// row it may touch, up to one tile past N, must sit below 2^31 bytes.
+bool pipe_offsets_fit(const FwdArgs& a, int bc) {
+  const int64_t lim = INT64_C(1) << 31;
+  return ((int64_t)a.N + bc) * a.k_sr * 2 < lim && ((int64_t)a.N + bc) * a.v_sr * 2 < lim;
+}
+
+// Variant choice, from measurements on MI355X: d=64 runs the pipelined
+// kernel with 8 waves (256 query rows) per workgroup; d=128 the register-
+// staged kernel with 8 waves (the pipelined one spills at d=128); d=96 and
+// d=256 the register-staged kernel.
 template <int D, int DT, bool CAUSAL>
 int pick(FwdArgs a, hipStream_t st) {
+  if constexpr (D == 64) {
+    if (pipe_offsets_fit(a, 64)) return launch_pipe<D, DT, CAUSAL, 8, 1, 64>(a, st);
+  }
   if constexpr (D == 256)
     return launch_one<D, DT, CAUSAL, 4, 1, 32>(a, st);
+  else if constexpr (D == 128)
+    return launch_one<D, DT, CAUSAL, 8, 1, 64>(a, st);
   else
     return launch_one<D, DT, CAUSAL, 4, 1, 64>(a, st);
 }
