@@ -43,14 +43,21 @@ bool pipe_offsets_fit(const FwdArgs& a, int bc) {
   return ((int64_t)a.N + bc) * a.k_sr * 2 < lim && ((int64_t)a.N + bc) * a.v_sr * 2 < lim;
 }
 
-// Variant choice, from measurements on MI355X: d=64 runs the pipelined
-// kernel with 8 waves (256 query rows) per workgroup; d=128 the register-
-// staged kernel with 8 waves (the pipelined one spills at d=128); d=96 and
-// d=256 the register-staged kernel.
+// Variant choice, from measurements on MI355X (kernel time per launch):
+//  d=64:  the pipelined kernel with 8 waves for long sequences (N=6400:
+//         241 us, N=4096: 349 us) and 4 waves for short ones (N=400: 16.5 us);
+//  d=128: the register-staged kernel with 8 waves (N=8192 causal: 620 us;
+//         the pipelined kernel spills at d=128);
+//  d=96, d=256: the register-staged kernel with 4 waves.
+// The LDS-resident short-sequence kernel (fa_fwd_short.h) measured slower than
+// these at N=400 and is kept out of the dispatch.
 template <int D, int DT, bool CAUSAL>
 int pick(FwdArgs a, hipStream_t st) {
   if constexpr (D == 64) {
-    if (pipe_offsets_fit(a, 64)) return launch_pipe<D, DT, CAUSAL, 8, 1, 64>(a, st);
+    if (pipe_offsets_fit(a, 64)) {
+      if (a.N <= 1024) return launch_pipe<D, DT, CAUSAL, 4, 1, 64>(a, st);
+      return launch_pipe<D, DT, CAUSAL, 8, 1, 64>(a, st);
+    }
   }
   if constexpr (D == 256)
     return launch_one<D, DT, CAUSAL, 4, 1, 32>(a, st);

@@ -221,9 +221,9 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
     const int r = qw0 + 32 * j + l32;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (r < Nb) x = *(const u32x4*)(Qg + r * a.q_sr + 16 * kk + 8 * hh);
-      qf[j][kk] = x ^ a.qsign;
+      // rows past the end load row Nb-1 (in bounds) and are zeroed
+      const u32x4 x = *(const u32x4*)(Qg + min(r, Nb - 1) * a.q_sr + 16 * kk + 8 * hh);
+      qf[j][kk] = (r < Nb ? x : u32x4{0u, 0u, 0u, 0u}) ^ a.qsign;
     }
   }
 

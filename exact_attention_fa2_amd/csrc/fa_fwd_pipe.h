@@ -69,7 +69,7 @@ __device__ __forceinline__ void tile_dma(__amdgpu_buffer_rsrc_t rs, int64_t row_
 }
 
 __device__ __forceinline__ void wait_dma_and_sync() {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA loads have landed
   __syncthreads();
 }
 
@@ -264,9 +264,9 @@ __global__ __launch_bounds__(NW * 64, MINW) void fa_fwd_pipe_kernel(const FwdArg
     const int r = qw0 + 32 * j + wv.l32;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (r < Nb) x = *(const u32x4*)(Qg + r * a.q_sr + 16 * kk + 8 * wv.hh);
-      qf[j][kk] = x ^ a.qsign;
+      // rows past the end load row Nb-1 (in bounds) and are zeroed
+      const u32x4 x = *(const u32x4*)(Qg + min(r, Nb - 1) * a.q_sr + 16 * kk + 8 * wv.hh);
+      qf[j][kk] = (r < Nb ? x : u32x4{0u, 0u, 0u, 0u}) ^ a.qsign;
     }
   }
 
