@@ -100,6 +100,8 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--eager", action="store_true", help="launch from Python each step (no graph)")
     ap.add_argument("--warm-cache", action="store_true", help="one input set (cache-resident)")
+    ap.add_argument("--impl", default="fa2", choices=["fa2", "fa1_order"],
+                    help="fa2: fa_fwd (default); fa1_order: the FlashAttention-1 loop-order ablation")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="run only a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -141,10 +143,16 @@ def main() -> int:
         lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
         sets.append((q, k, v, o, lse))
     stream = torch.cuda.Stream()
+    ws = None
+    if args.impl == "fa1_order":
+        ws = torch.empty(fa.fa_fwd_fa1_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
 
     def launch(i):
         q, k, v, o, lse = sets[i % R]
-        fa.fa_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.d, w.scale, w.causal)
+        if ws is None:
+            fa.fa_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.d, w.scale, w.causal)
+        else:
+            fa.fa_fwd_fa1_order(q, k, v, o, lse, ws, w.B, w.H, w.N, w.d, w.scale, w.causal)
 
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
@@ -207,15 +215,16 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
-                   "input_sets": R, "graph": graph is not None, "parallelism": "none (1 GPU)"},
+                   "input_sets": R, "graph": graph is not None, "impl": args.impl,
+                   "parallelism": "none (1 GPU)"},
         "roofline": {
             "bound": bound,
             "achieved": round(achieved, 2),
             "peak": peak,
             "unit": unit,
             "frac": round(achieved / peak, 4),
-            "traffic": stored_traffic(w.name),
-            "kernel": "fa_fwd_kernel",
+            "traffic": stored_traffic(w.name) if args.impl == "fa2" else None,
+            "kernel": "fa_fwd_fa1_kernel" if ws is not None else "fa_fwd",
             "kernel_us": round(kern_s * 1e6, 3),
             "alg_bytes": abytes,
             "alg_flop": aflops,

@@ -9,6 +9,7 @@
 #include <cstring>
 
 #include "fa.h"
+#include "fa_check.h"
 #include "fa_fwd_kernel.h"
 #include "fa_launch.h"
 
@@ -71,6 +72,28 @@ void fill_scale(FwdArgs& a, float scale) {
   a.qsign = scale < 0.f ? 0x80008000u : 0u;
 }
 
+FwdArgs contiguous_args(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                        int N, int d, float scale) {
+  FwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  const int64_t sr = d, sh = (int64_t)N * d, sb = (int64_t)H * N * d;
+  a.q_sb = a.k_sb = a.v_sb = a.o_sb = sb;
+  a.q_sh = a.k_sh = a.v_sh = a.o_sh = sh;
+  a.q_sr = a.k_sr = a.v_sr = a.o_sr = sr;
+  a.lse_sb = (int64_t)H * N;
+  a.lse_sh = N;
+  a.cu_seqlens = nullptr;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  fill_scale(a, scale);
+  return a;
+}
+
 }  // namespace fa
 
 using namespace fa;
@@ -112,23 +135,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     return FA_ERR_ALIAS;
   if ((rc = device_ok()) != FA_OK) return rc;
 
-  FwdArgs a{};
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
-  a.o = static_cast<uint16_t*>(o);
-  a.lse = lse;
-  const int64_t sr = d, sh = (int64_t)N * d, sb = (int64_t)H * N * d;
-  a.q_sb = a.k_sb = a.v_sb = a.o_sb = sb;
-  a.q_sh = a.k_sh = a.v_sh = a.o_sh = sh;
-  a.q_sr = a.k_sr = a.v_sr = a.o_sr = sr;
-  a.lse_sb = (int64_t)H * N;
-  a.lse_sh = N;
-  a.cu_seqlens = nullptr;
-  a.B = B;
-  a.H = H;
-  a.N = N;
-  fill_scale(a, scale);
+  const FwdArgs a = contiguous_args(q, k, v, o, lse, B, H, N, d, scale);
   return launch_fwd(a, d, dtype, causal != 0, static_cast<hipStream_t>(stream));
 }
 

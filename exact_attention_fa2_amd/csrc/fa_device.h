@@ -48,6 +48,18 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   }
 }
 
+// acc + lo + hi of a packed pair of 16-bit values, with fp32 accumulation
+// (v_dot2_f32_f16 / v_dot2_f32_bf16 against (1, 1))
+template <int DT>
+__device__ __forceinline__ float dot2_sum(uint32_t packed, float acc) {
+  if constexpr (DT == DT_F16)
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, packed), h16x2{(_Float16)1.f, (_Float16)1.f},
+                                  acc, false);
+  else
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b16x2, packed),
+                                           b16x2{(__bf16)1.f, (__bf16)1.f}, acc, false);
+}
+
 template <int DT>
 __device__ __forceinline__ float to_f32(uint16_t x) {
   if constexpr (DT == DT_F16)

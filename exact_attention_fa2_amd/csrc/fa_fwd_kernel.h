@@ -74,7 +74,7 @@ __device__ __forceinline__ void tile_step_fwd(bool masked, const uint16_t* __res
                                                const uint16_t* __restrict__ sv, int key0, int Nb,
                                                int qw0, int lane, float c, const u32x4 (&qf)[QB][D / 16],
                                                f32x16 (&oacc)[QB][D / 32], float (&m_run)[QB],
-                                               float (&l_run)[QB]) {
+                                               float (&l_run)[2][QB]) {
   constexpr int KK = D / 16, DB = D / 32, KB = BC / 32;
   const int l32 = lane & 31, hh = lane >> 5;
 
@@ -124,7 +124,8 @@ __device__ __forceinline__ void tile_step_fwd(bool masked, const uint16_t* __res
     const float m_new = fmaxf(m_run[j], mx * c);
     if (wave_any(m_new > m_run[j] + kRescaleGap)) {
       const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[j] - m_new);
-      l_run[j] *= alpha;
+      l_run[0][j] *= alpha;
+      l_run[1][j] *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -132,7 +133,9 @@ __device__ __forceinline__ void tile_step_fwd(bool masked, const uint16_t* __res
       m_run[j] = m_new;
     }
     const float mref = (m_run[j] == -INFINITY) ? 0.f : m_run[j];
-    float lsum = 0.f;
+    // l[0]: sum of the 16-bit weights that multiply V (normalises O exactly
+    // like the product it divides); l[1]: fp32 sum for the bf16 LSE
+    float lp[4] = {0.f, 0.f, 0.f, 0.f}, lf[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       float p[16];
@@ -140,19 +143,21 @@ __device__ __forceinline__ void tile_step_fwd(bool masked, const uint16_t* __res
       for (int r = 0; r < 16; ++r) {
         // c > 0 always (clamped on the host), so a masked -inf stays -inf
         p[r] = fast_exp2(__builtin_fmaf(s[kb][j][r], c, -mref));
-        lsum += p[r];
+        if constexpr (DT == DT_BF16) lf[r & 3] += p[r];
       }
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
         u32x4 x;
-        x[0] = pack2<DT>(p[8 * c2 + 0], p[8 * c2 + 1]);
-        x[1] = pack2<DT>(p[8 * c2 + 2], p[8 * c2 + 3]);
-        x[2] = pack2<DT>(p[8 * c2 + 4], p[8 * c2 + 5]);
-        x[3] = pack2<DT>(p[8 * c2 + 6], p[8 * c2 + 7]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] = pack2<DT>(p[8 * c2 + 2 * e], p[8 * c2 + 2 * e + 1]);
+          lp[e] = dot2_sum<DT>(x[e], lp[e]);
+        }
         pf[j][2 * kb + c2] = x;
       }
     }
-    l_run[j] += lsum;
+    l_run[0][j] += (lp[0] + lp[1]) + (lp[2] + lp[3]);
+    if constexpr (DT == DT_BF16) l_run[1][j] += (lf[0] + lf[1]) + (lf[2] + lf[3]);
   }
 
   // Oᵀ += Vᵀ Pᵀ ; k-slot 8*hh + 4*rd + e of chunk ci is key 16*ci + 8*rd + 4*hh + e
@@ -268,9 +273,9 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[j][db][r] = 0.f;
-  float m_run[QB], l_run[QB];
+  float m_run[QB], l_run[2][QB];
 #pragma unroll
-  for (int j = 0; j < QB; ++j) { m_run[j] = -INFINITY; l_run[j] = 0.f; }
+  for (int j = 0; j < QB; ++j) { m_run[j] = -INFINITY; l_run[0][j] = 0.f; l_run[1][j] = 0.f; }
 
   fetch(0);
   stash(0);
@@ -292,7 +297,8 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
-    const float l_tot = l_run[j] + xor_lane32(l_run[j]);
+    const float l_tot = l_run[0][j] + xor_lane32(l_run[0][j]);
+    const float l_lse = DT == DT_F16 ? l_tot : l_run[1][j] + xor_lane32(l_run[1][j]);
     const float inv = 1.f / l_tot;
     const int qrow = qw0 + 32 * j + l32;
     if (qrow < Nb) {
@@ -306,7 +312,7 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
           x[1] = pack2<DT>(oacc[j][db][4 * g4 + 2] * inv, oacc[j][db][4 * g4 + 3] * inv);
           *(u32x2*)(orow + db * 32 + 8 * g4 + 4 * hh) = x;
         }
-      if (hh == 0) Lg[qrow] = (m_run[j] + fast_log2(l_tot)) * kLn2;
+      if (hh == 0) Lg[qrow] = (m_run[j] + fast_log2(l_lse)) * kLn2;
     }
   }
 }

@@ -133,31 +133,36 @@ struct PipeWave {
     }
   }
 
-  // P = exp2(S c - m) packed to 16 bits, and its fp32 row sums (four
-  // independent partial sums keep the dependency chains short)
+  // P = exp2(S c - m) packed to 16 bits. l[0] sums the packed weights (the
+  // exact normaliser of the product they enter); l[1] is the fp32 sum the
+  // bf16 LSE needs (fp16 weights are accurate enough for both).
   __device__ __forceinline__ void probs(const f32x16 (&s)[KB][QB], const float (&m_run)[QB],
-                                        u32x4 (&pf)[QB][BC / 16], float (&l_run)[QB]) const {
+                                        u32x4 (&pf)[QB][BC / 16], float (&l_run)[2][QB]) const {
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
       const float mref = (m_run[j] == -INFINITY) ? 0.f : m_run[j];
-      float ls[4] = {0.f, 0.f, 0.f, 0.f};
+      float lp[4] = {0.f, 0.f, 0.f, 0.f}, lf[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         float p[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           p[r] = fast_exp2(__builtin_fmaf(s[kb][j][r], c, -mref));
-          ls[r & 3] += p[r];
+          if constexpr (DT == DT_BF16) lf[r & 3] += p[r];
         }
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
           u32x4 x;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = pack2<DT>(p[8 * c2 + 2 * e], p[8 * c2 + 2 * e + 1]);
+          for (int e = 0; e < 4; ++e) {
+            x[e] = pack2<DT>(p[8 * c2 + 2 * e], p[8 * c2 + 2 * e + 1]);
+            lp[e] = dot2_sum<DT>(x[e], lp[e]);
+          }
           pf[j][2 * kb + c2] = x;
         }
       }
-      l_run[j] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      l_run[0][j] += (lp[0] + lp[1]) + (lp[2] + lp[3]);
+      if constexpr (DT == DT_BF16) l_run[1][j] += (lf[0] + lf[1]) + (lf[2] + lf[3]);
     }
   }
 
@@ -184,13 +189,14 @@ struct PipeWave {
   // raise the running max when it grew by more than kRescaleGap, rescaling
   // the accumulator and the running sum by exp2(m_old - m_new)
   __device__ __forceinline__ void update_max(const float (&mx)[QB], float (&m_run)[QB],
-                                             float (&l_run)[QB], f32x16 (&oacc)[QB][DB]) const {
+                                             float (&l_run)[2][QB], f32x16 (&oacc)[QB][DB]) const {
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
       const float m_new = fmaxf(m_run[j], mx[j]);
       if (wave_any(m_new > m_run[j] + kRescaleGap)) {
         const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[j] - m_new);
-        l_run[j] *= alpha;
+        l_run[0][j] *= alpha;
+        l_run[1][j] *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -277,9 +283,9 @@ __global__ __launch_bounds__(NW * 64, MINW) void fa_fwd_pipe_kernel(const FwdArg
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[j][db][r] = 0.f;
-  float m_run[QB], l_run[QB], mx[QB];
+  float m_run[QB], l_run[2][QB], mx[QB];
 #pragma unroll
-  for (int j = 0; j < QB; ++j) { m_run[j] = -INFINITY; l_run[j] = 0.f; }
+  for (int j = 0; j < QB; ++j) { m_run[j] = -INFINITY; l_run[0][j] = 0.f; l_run[1][j] = 0.f; }
 
   auto needs_mask = [&](int t) __attribute__((always_inline)) { return (t + 1) * BC > Nb || (CAUSAL && t * BC + BC - 1 > qw0); };
 
@@ -335,7 +341,8 @@ __global__ __launch_bounds__(NW * 64, MINW) void fa_fwd_pipe_kernel(const FwdArg
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
-    const float l_tot = l_run[j] + xor_lane32(l_run[j]);
+    const float l_tot = l_run[0][j] + xor_lane32(l_run[0][j]);
+    const float l_lse = DT == DT_F16 ? l_tot : l_run[1][j] + xor_lane32(l_run[1][j]);
     const float inv = 1.f / l_tot;
     const int qrow = qw0 + 32 * j + wv.l32;
     if (qrow < Nb) {
@@ -349,7 +356,7 @@ __global__ __launch_bounds__(NW * 64, MINW) void fa_fwd_pipe_kernel(const FwdArg
           x[1] = pack2<DT>(oacc[j][db][4 * g4 + 2] * inv, oacc[j][db][4 * g4 + 3] * inv);
           *(u32x2*)(orow + db * 32 + 8 * g4 + 4 * wv.hh) = x;
         }
-      if (wv.hh == 0) Lg[qrow] = (m_run[j] + fast_log2(l_tot)) * kLn2;
+      if (wv.hh == 0) Lg[qrow] = (m_run[j] + fast_log2(l_lse)) * kLn2;
     }
   }
 }

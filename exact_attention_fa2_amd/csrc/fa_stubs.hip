@@ -6,9 +6,4 @@ int fa_bwd(const void*, const void*, const void*, const void*, const void*, cons
   return FA_ERR_UNSUPPORTED;
 }
 int64_t fa_bwd_workspace_bytes(int, int, int, int) { return -1; }
-int fa_fwd_fa1_order(const void*, const void*, const void*, void*, float*, void*, int, int, int,
-                     int, float, int, int, void*) {
-  return FA_ERR_UNSUPPORTED;
-}
-int64_t fa_fwd_fa1_workspace_bytes(int, int, int, int) { return -1; }
 }

@@ -136,3 +136,21 @@ def test_python_binding_rejects_cpu_tensors(L):
         fa.attention(q, q, q)
     with pytest.raises(TypeError):
         fa._dtype_code(torch.zeros(1, dtype=torch.float32))
+
+
+def test_fa1_order_argument_errors(L):
+    def call(**kw):
+        a = dict(q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 256 * MB, ws=A + 512 * MB,
+                 B=1, H=2, N=64, d=64, scale=0.125, causal=0, dtype=0)
+        a.update(kw)
+        return L.fa_fwd_fa1_order(a["q"], a["k"], a["v"], a["o"], a["lse"], a["ws"], a["B"], a["H"], a["N"],
+                                  a["d"], a["scale"], a["causal"], a["dtype"], None)
+    assert call(ws=None) == NULL
+    assert call(ws=A + 512 * MB + 4) == ALIGN
+    assert call(ws=A + 192 * MB) == ALIAS  # workspace over o
+    assert call(d=72) == UNSUP
+    assert call(B=0, ws=None) == OK
+    assert L.fa_fwd_fa1_workspace_bytes(1, 2, 64, 64) > 0
+    assert L.fa_fwd_fa1_workspace_bytes(1, 2, 0, 64) == 0
+    assert L.fa_fwd_fa1_workspace_bytes(1, -2, 64, 64) == -1
+    assert L.fa_fwd_fa1_workspace_bytes(1, 2, 64, 80) == -1
