@@ -43,28 +43,29 @@ bool pipe_offsets_fit(const FwdArgs& a, int bc) {
   return ((int64_t)a.N + bc) * a.k_sr * 2 < lim && ((int64_t)a.N + bc) * a.v_sr * 2 < lim;
 }
 
-// Variant choice, from measurements on MI355X (kernel time per launch):
-//  d=64:  the pipelined kernel with 8 waves for long sequences (N=6400:
-//         241 us, N=4096: 349 us) and 4 waves for short ones (N=400: 16.5 us);
-//  d=128: the register-staged kernel with 8 waves (N=8192 causal: 620 us;
-//         the pipelined kernel spills at d=128);
-//  d=96, d=256: the register-staged kernel with 4 waves.
-// The LDS-resident short-sequence kernel (fa_fwd_short.h) measured slower than
-// these at N=400 and is kept out of the dispatch.
+// Variant choice, from same-run measurements on MI355X (kernel time per
+// launch): the register-staged kernel with 8 waves (256 query rows) per
+// workgroup is fastest whenever the grid fills the chip (N=6400 d64: 219 us,
+// N=4096 d64: 310 us, N=400 x128 heads: 16.5 us, N=8192 causal d128: 640 us);
+// when B*H*ceil(N/256) is below the 256 CUs, the pipelined LDS-DMA kernel
+// with 4 waves (128 rows) halves the rows per workgroup for more parallelism
+// (N=400 x4 heads: 10.0 us vs 13.0 us); at d=128 (where the pipelined kernel
+// spills) the register-staged one with 4 waves. d=256 uses 32-key tiles.
 template <int D, int DT, bool CAUSAL>
 int pick(FwdArgs a, hipStream_t st) {
+  const int64_t wg256 = (int64_t)a.B * a.H * ((a.N + 255) / 256);
   if constexpr (D == 64) {
-    if (pipe_offsets_fit(a, 64)) {
-      if (a.N <= 1024) return launch_pipe<D, DT, CAUSAL, 4, 1, 64>(a, st);
-      return launch_pipe<D, DT, CAUSAL, 8, 1, 64>(a, st);
-    }
+    if (wg256 < 256 && pipe_offsets_fit(a, 64)) return launch_pipe<D, DT, CAUSAL, 4, 1, 64>(a, st);
+  }
+  if constexpr (D == 128) {
+    if (wg256 < 256) return launch_one<D, DT, CAUSAL, 4, 1, 64>(a, st);
   }
   if constexpr (D == 256)
     return launch_one<D, DT, CAUSAL, 4, 1, 32>(a, st);
-  else if constexpr (D == 128)
-    return launch_one<D, DT, CAUSAL, 8, 1, 64>(a, st);
-  else
+  else if constexpr (D == 96)
     return launch_one<D, DT, CAUSAL, 4, 1, 64>(a, st);
+  else
+    return launch_one<D, DT, CAUSAL, 8, 1, 64>(a, st);
 }
 
 template <int D, int DT>
