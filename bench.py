@@ -100,8 +100,9 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--eager", action="store_true", help="launch from Python each step (no graph)")
     ap.add_argument("--warm-cache", action="store_true", help="one input set (cache-resident)")
-    ap.add_argument("--impl", default="fa2", choices=["fa2", "fa1_order"],
-                    help="fa2: fa_fwd (default); fa1_order: the FlashAttention-1 loop-order ablation")
+    ap.add_argument("--impl", default="fa2", choices=["fa2", "fa1_order", "bwd"],
+                    help="fa2: fa_fwd (default); fa1_order: the FlashAttention-1 loop-order "
+                         "ablation; bwd: fa_bwd (the backward by recomputation)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="run only a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -132,6 +133,13 @@ def main() -> int:
     abytes = acc.alg_bytes(w.B, w.H, w.N, w.d, elem)
     aflops = acc.alg_flops(w.B, w.H, w.N, w.d, w.causal)
     mflops = acc.metric_flops(w.B, w.H, w.N, w.d)
+    metric = METRIC
+    if args.impl == "bwd":
+        # backward: five N x N x d products (S, dP, dV, dK, dQ) = 2.5x the forward;
+        # bytes: read Q, K, V, O, dO and LSE, write dQ, dK, dV
+        aflops, mflops = int(2.5 * aflops), int(2.5 * mflops)
+        abytes = acc.alg_bytes_bwd(w.B, w.H, w.N, w.d, elem)
+        metric = "attn bwd TFLOP/s (2.5 x 4·B·H·N²·d)"
     R = 1 if args.warm_cache else max(1, math.ceil(ROTATE_BYTES / abytes))
     log(f"workload {w.name}: {w.describe()}; {R} rotating input sets; alg bytes {abytes/1e6:.2f} MB, "
         f"alg flop {aflops/1e9:.2f} G")
@@ -144,21 +152,33 @@ def main() -> int:
         sets.append((q, k, v, o, lse))
     stream = torch.cuda.Stream()
     ws = None
+    grads = []
     if args.impl == "fa1_order":
         ws = torch.empty(fa.fa_fwd_fa1_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+    elif args.impl == "bwd":
+        ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+        for r, (q, k, v, o, lse) in enumerate(sets):
+            fa.fa_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.d, w.scale, w.causal)  # O, LSE (untimed)
+            do = inputs.make_like(q.cpu(), 1000 + r).to(dev)
+            grads.append((do, torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)))
+        torch.cuda.synchronize()
 
     def launch(i):
         q, k, v, o, lse = sets[i % R]
-        if ws is None:
+        if args.impl == "fa2":
             fa.fa_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.d, w.scale, w.causal)
-        else:
+        elif args.impl == "fa1_order":
             fa.fa_fwd_fa1_order(q, k, v, o, lse, ws, w.B, w.H, w.N, w.d, w.scale, w.causal)
+        else:
+            do, dq, dk, dv = grads[i % R]
+            fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, w.B, w.H, w.N, w.d, w.scale, w.causal)
 
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
             launch(i)
     torch.cuda.synchronize()
-    ref_o = sets[0][3].clone()
+    out_idx = sets[0][3] if args.impl != "bwd" else grads[0][1]
+    ref_o = out_idx.clone()
 
     K = args.steps
     graph = None
@@ -170,7 +190,7 @@ def main() -> int:
         torch.cuda.synchronize()
         graph.replay()  # untimed replay: check the graph reproduces the eager output
         torch.cuda.synchronize()
-        if not torch.equal(sets[0][3], ref_o):
+        if not torch.equal(out_idx, ref_o):
             log("graph replay disagrees with the eager launch")
             return 1
 
@@ -202,7 +222,7 @@ def main() -> int:
         f"{aflops/kern_s/1e12:.1f} TFLOP/s alg, {abytes/kern_s/1e9:.0f} GB/s alg")
 
     out = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -224,7 +244,8 @@ def main() -> int:
             "unit": unit,
             "frac": round(achieved / peak, 4),
             "traffic": stored_traffic(w.name) if args.impl == "fa2" else None,
-            "kernel": "fa_fwd_fa1_kernel" if ws is not None else "fa_fwd",
+            "kernel": {"fa2": "fa_fwd", "fa1_order": "fa_fwd_fa1_kernel",
+                       "bwd": "fa_bwd (dot + dK/dV + dQ kernels)"}[args.impl],
             "kernel_us": round(kern_s * 1e6, 3),
             "alg_bytes": abytes,
             "alg_flop": aflops,

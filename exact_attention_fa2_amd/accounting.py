@@ -31,6 +31,11 @@ def alg_bytes(B: int, H: int, N: int, d: int, elem_bytes: int = 2) -> int:
     return 4 * B * H * N * d * elem_bytes + 4 * B * H * N
 
 
+def alg_bytes_bwd(B: int, H: int, N: int, d: int, elem_bytes: int = 2) -> int:
+    """Backward: read Q, K, V, O, dO and LSE once; write dQ, dK, dV once."""
+    return 8 * B * H * N * d * elem_bytes + 4 * B * H * N
+
+
 def num_tiles(n: int, block: int) -> int:
     """Blocks of ``block`` rows needed to cover ``n`` rows (last one ragged)."""
     return (n + block - 1) // block

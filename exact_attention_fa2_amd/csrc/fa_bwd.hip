@@ -1,0 +1,106 @@
+// C ABI of the backward pass (fa_bwd, fa_bwd_workspace_bytes).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "fa.h"
+#include "fa_bwd_kernel.h"
+#include "fa_check.h"
+
+namespace fa {
+namespace {
+
+int64_t bwd_bytes(int B, int H, int N) {
+  return ((int64_t)B * H * N * 4 + 255) / 256 * 256;  // D_i in fp32
+}
+
+template <int D, int DT, bool CAUSAL>
+int launch(const BwdArgs& a, hipStream_t st) {
+  const int64_t rows = (int64_t)a.B * a.H * a.N;
+  const int64_t gdot = (rows + 255) / 256;
+  const int64_t gk = (int64_t)a.B * a.H * ((a.N + 127) / 128);
+  if (gdot > (INT64_C(1) << 31) - 1 || gk > (INT64_C(1) << 31) - 1) return FA_ERR_DIM;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL((fa_bwd_dot_kernel<D, DT>), dim3((unsigned)gdot), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, DT, CAUSAL>), dim3((unsigned)gk), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, DT, CAUSAL>), dim3((unsigned)gk), dim3(256), 0, st, a);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+template <int D, int DT>
+int pick_c(const BwdArgs& a, bool causal, hipStream_t st) {
+  return causal ? launch<D, DT, true>(a, st) : launch<D, DT, false>(a, st);
+}
+
+template <int DT>
+int pick_d(const BwdArgs& a, int d, bool causal, hipStream_t st) {
+  switch (d) {
+    case 64: return pick_c<64, DT>(a, causal, st);
+    case 96: return pick_c<96, DT>(a, causal, st);
+    case 128: return pick_c<128, DT>(a, causal, st);
+    default: return FA_ERR_UNSUPPORTED;  // d = 256: the dK/dV accumulators do not fit
+  }
+}
+
+}  // namespace
+}  // namespace fa
+
+using namespace fa;
+
+extern "C" {
+
+int64_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
+  int64_t elems = 0;
+  if (check_problem(B, H, N, d, 1.f, FA_F16, &elems) != FA_OK) return -1;
+  if (elems == 0) return 0;
+  return bwd_bytes(B, H, N);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* do_, const float* lse,
+           void* dq, void* dk, void* dv, void* workspace, int B, int H, int N, int d, float scale,
+           int causal, int dtype, void* stream) {
+  int64_t elems = 0;
+  int rc = check_problem(B, H, N, d, scale, dtype, &elems);
+  if (rc != FA_OK) return rc;
+  if (d == 256) return FA_ERR_UNSUPPORTED;
+  if (elems == 0) return FA_OK;
+  if (!q || !k || !v || !o || !do_ || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
+  const void* a16[8] = {q, k, v, o, do_, dq, dk, dv};
+  for (const void* p : a16)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  if (!aligned16(workspace) || (reinterpret_cast<uintptr_t>(lse) & 3)) return FA_ERR_ALIGN;
+  const int64_t nb = elems * 2, lb = (elems / d) * 4, wb = bwd_bytes(B, H, N);
+  const void* ins[6] = {q, k, v, o, do_, lse};
+  const int64_t insz[6] = {nb, nb, nb, nb, nb, lb};
+  void* outs[4] = {dq, dk, dv, workspace};
+  const int64_t outsz[4] = {nb, nb, nb, wb};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlap(outs[i], outsz[i], ins[j], insz[j])) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return FA_ERR_ALIAS;
+  }
+  if ((rc = device_ok()) != FA_OK) return rc;
+
+  BwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<const uint16_t*>(o);
+  a.dout = static_cast<const uint16_t*>(do_);
+  a.lse = lse;
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.dvec = static_cast<float*>(workspace);
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.c = std::fmax(std::fabs(scale) * kLog2e, 1e-30f);
+  a.scale = scale;
+  a.qsign = scale < 0.f ? 0x80008000u : 0u;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return dtype == FA_BF16 ? pick_d<DT_BF16>(a, d, causal != 0, st) : pick_d<DT_F16>(a, d, causal != 0, st);
+}
+
+}  // extern "C"

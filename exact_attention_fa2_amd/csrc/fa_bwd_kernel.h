@@ -1,0 +1,409 @@
+// Attention backward by recomputation for gfx950 ("FlashAttention explainer"
+// (aitangshan.cn) section 6.2, first strategy; "YOLO11 attention swapped for a
+// FlashAttention-2-style implementation" (discosf.com) section 2.3): only Q,
+// K, V, O, dO and the forward's LSE are read; S and P are rebuilt tile by tile
+// from LSE and never stored. With P = exp(s - LSE) and dP = dO Vᵀ:
+//   dV = Pᵀ dO,  dS = P ∘ (dP - D),  D_i = <dO_i, O_i>,
+//   dK = scale · dSᵀ Q,  dQ = scale · dS K.
+//
+// MI355X layout (our design): three kernels and no atomics.
+//  * fa_bwd_dot_kernel: D_i in fp32.
+//  * fa_bwd_dkdv_kernel: one workgroup per block of 128 keys, each wave owning
+//    32 keys whose K and V fragments stay in registers; 64-query tiles of Q,
+//    dO, LSE and D stream through LDS. S and dP are computed with the key in
+//    the lane (S = Q Kᵀ), so P and dS are directly the B operand of
+//    dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS, whose A operands (dOᵀ, Qᵀ) come from the
+//    row-major LDS tiles through the transposing LDS read.
+//  * fa_bwd_dq_kernel: the mirror image with the query in the lane (like the
+//    forward): Pᵀ = exp2(Sᵀ c - LSE log2 e), dPᵀ = V dOᵀ, dQᵀ += Kᵀ dSᵀ.
+#pragma once
+#include "fa_fwd_kernel.h"
+
+namespace fa {
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* dvec;   // D_i, [B, H, N] fp32 (workspace)
+  int B, H, N;
+  float c;       // |scale| * log2(e), > 0
+  float scale;   // signed scale (multiplies dQ and dK)
+  uint32_t qsign;  // 0x80008000 when scale < 0 (Q is read sign-flipped)
+};
+
+// ---- D_i = <dO_i, O_i> ----
+template <int D, int DT>
+__global__ __launch_bounds__(256) void fa_bwd_dot_kernel(const BwdArgs a) {
+  const int64_t rows = (int64_t)a.B * a.H * a.N;
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= rows) return;
+  const uint16_t* op = a.o + r * D;
+  const uint16_t* gp = a.dout + r * D;
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < D; c += 8) {
+    const u32x4 x = *(const u32x4*)(op + c);
+    const u32x4 y = *(const u32x4*)(gp + c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc += to_f32<DT>((uint16_t)(x[e] & 0xFFFF)) * to_f32<DT>((uint16_t)(y[e] & 0xFFFF));
+      acc += to_f32<DT>((uint16_t)(x[e] >> 16)) * to_f32<DT>((uint16_t)(y[e] >> 16));
+    }
+  }
+  a.dvec[r] = acc;
+}
+
+template <int D>
+struct BwdSmem {
+  static constexpr int BQ = 64;        // query rows per tile (dK/dV kernel)
+  static constexpr int STR = D + 16;   // padded row (halves)
+  static constexpr int TILE = BQ * STR;
+  // per stage: Q tile, dO tile, LSE·log2e, D
+  static constexpr int STAGE_HALVES = 2 * TILE + 2 * BQ * 2;
+};
+
+// 16 per-register row values for rows 8*(r/4) + 4*hh + r%4 of a 32-row block
+// starting at `base` of an fp32 LDS vector
+__device__ __forceinline__ void load_rowvals(const float* base, int hh, float (&v)[16]) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const f32x4 x = *(const f32x4*)(base + 8 * g + 4 * hh);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[4 * g + e] = x[e];
+  }
+}
+
+// ---- dK, dV: one workgroup per 128 keys ----
+template <int D, int DT, bool CAUSAL>
+__global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(const BwdArgs a) {
+  constexpr int NW = 4, NT = 256, KK = D / 16, DB = D / 32;
+  using SM = BwdSmem<D>;
+  constexpr int BQ = SM::BQ, STR = SM::STR;
+  constexpr int CH = BQ * D / 8 / NT;  // 16-byte chunks per thread per tile
+  static_assert(BQ * D / 8 % NT == 0, "tile must split evenly");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SM::STAGE_HALVES];
+
+  const int nkb = (a.N + 127) / 128;
+  const int bh = blockIdx.x / nkb, kblk = blockIdx.x - bh * nkb;
+  if (bh >= a.B * a.H) return;
+  const int64_t off = (int64_t)bh * a.N * D;
+  const uint16_t* Qg = a.q + off;
+  const uint16_t* Kg = a.k + off;
+  const uint16_t* Vg = a.v + off;
+  const uint16_t* Gg = a.dout + off;
+  const float* Lg = a.lse + (int64_t)bh * a.N;
+  const float* Dg = a.dvec + (int64_t)bh * a.N;
+  const int N = a.N;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int kw0 = kblk * 128 + w * 32;  // first key of this wave
+  const int krow = kw0 + l32;
+
+  // K and V fragments of this wave's keys (B operands: key in the lane)
+  u32x4 kf[KK], vf[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const int rr = min(krow, N - 1);
+    const u32x4 xk = *(const u32x4*)(Kg + (int64_t)rr * D + 16 * kk + 8 * hh);
+    const u32x4 xv = *(const u32x4*)(Vg + (int64_t)rr * D + 16 * kk + 8 * hh);
+    kf[kk] = krow < N ? xk : u32x4{0u, 0u, 0u, 0u};
+    vf[kk] = krow < N ? xv : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { dk[db][r] = 0.f; dv[db][r] = 0.f; }
+
+  // query tiles: causal blocks start at the tile holding the first key
+  const int t0 = CAUSAL ? (kblk * 128) / BQ : 0;
+  const int nt = (N + BQ - 1) / BQ;
+
+  u32x4 qs[CH], gs[CH];
+  float ls = 0.f, ds = 0.f;
+  auto fetch = [&](int t) __attribute__((always_inline)) {
+    const int q0 = t * BQ;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int ci = tid + NT * c;
+      const int r = ci / (D / 8), col = (ci % (D / 8)) * 8;
+      const int gr = min(q0 + r, N - 1);
+      const u32x4 x = *(const u32x4*)(Qg + (int64_t)gr * D + col);
+      const u32x4 y = *(const u32x4*)(Gg + (int64_t)gr * D + col);
+      qs[c] = q0 + r < N ? (x ^ a.qsign) : u32x4{0u, 0u, 0u, 0u};
+      gs[c] = q0 + r < N ? y : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (tid < BQ) {
+      const int gr = q0 + tid;
+      // rows past the end: a huge LSE makes their weights exactly zero
+      ls = gr < N ? Lg[gr] * kLog2e : INFINITY;
+      ds = gr < N ? Dg[gr] : 0.f;
+    }
+  };
+  auto stash = [&](int buf) __attribute__((always_inline)) {
+    uint16_t* sq = smem + buf * SM::STAGE_HALVES;
+    uint16_t* sg = sq + SM::TILE;
+    float* sl = (float*)(sg + SM::TILE);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int ci = tid + NT * c;
+      const int r = ci / (D / 8), col = (ci % (D / 8)) * 8;
+      *(u32x4*)(sq + r * STR + col) = qs[c];
+      *(u32x4*)(sg + r * STR + col) = gs[c];
+    }
+    if (tid < BQ) {
+      sl[tid] = ls;
+      sl[BQ + tid] = ds;
+    }
+  };
+
+  if (t0 < nt) {
+    fetch(t0);
+    stash(0);
+  }
+  const int g16 = lane >> 4, s16 = lane & 15;
+  for (int t = t0; t < nt; ++t) {
+    __syncthreads();
+    if (t + 1 < nt) fetch(t + 1);
+    const uint16_t* sq = smem + ((t - t0) & 1) * SM::STAGE_HALVES;
+    const uint16_t* sg = sq + SM::TILE;
+    const float* sl = (const float*)(sg + SM::TILE);
+    const int q0 = t * BQ;
+#pragma unroll
+    for (int qb = 0; qb < BQ / 32; ++qb) {
+      const int qr0 = q0 + 32 * qb;  // first query of this 32-row block
+      if (CAUSAL && qr0 + 31 < kw0) continue;  // every query precedes every key
+      // S = Q Kᵀ and dP = dO Vᵀ, key in the lane, queries in the registers
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const u32x4 qa = *(const u32x4*)(sq + (32 * qb + l32) * STR + 16 * kk + 8 * hh);
+        const u32x4 ga = *(const u32x4*)(sg + (32 * qb + l32) * STR + 16 * kk + 8 * hh);
+        s = mfma32x32x16<DT>(qa, kf[kk], s);
+        dp = mfma32x32x16<DT>(ga, vf[kk], dp);
+      }
+      float lq[16], dq[16];
+      load_rowvals(sl + 32 * qb, hh, lq);
+      load_rowvals(sl + BQ + 32 * qb, hh, dq);
+      const bool diag = CAUSAL && qr0 < kw0 + 31;
+      u32x4 pp[2], sp[2];
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float pv[2], sv[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int r = 8 * c2 + 2 * e + u;
+            float p = fast_exp2(__builtin_fmaf(s[r], a.c, -lq[r]));
+            if (CAUSAL && diag) {
+              const int qrow = qr0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+              if (krow > qrow) p = 0.f;
+            }
+            pv[u] = p;
+            sv[u] = p * (dp[r] - dq[r]);
+          }
+          pp[c2][e] = pack2<DT>(pv[0], pv[1]);
+          sp[c2][e] = pack2<DT>(sv[0], sv[1]);
+        }
+      }
+      // dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS ; k-slot 8*hh + 4*rd + e of chunk c2 is
+      // query 16*c2 + 8*rd + 4*hh + e of this block
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const int ra = 32 * qb + 16 * c2 + 4 * hh + (s16 >> 2);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int col = db * 32 + (g16 & 1) * 16 + 4 * (s16 & 3);
+          const u32x2 glo = lds_read_tr4(sg + ra * STR + col);
+          const u32x2 ghi = lds_read_tr4(sg + (ra + 8) * STR + col);
+          const u32x2 qlo = lds_read_tr4(sq + ra * STR + col);
+          const u32x2 qhi = lds_read_tr4(sq + (ra + 8) * STR + col);
+          dv[db] = mfma32x32x16<DT>(u32x4{glo[0], glo[1], ghi[0], ghi[1]}, pp[c2], dv[db]);
+          dk[db] = mfma32x32x16<DT>(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, sp[c2], dk[db]);
+        }
+      }
+    }
+    if (t + 1 < nt) stash((t + 1 - t0) & 1);
+  }
+
+  // dK = scale dSᵀ Q = |scale| dSᵀ Q' (Q' is Q with its sign folded in for a
+  // negative scale); dV = Pᵀ dO. Key row, 4 consecutive d per group.
+  if (krow < N) {
+    uint16_t* dkr = a.dk + off + (int64_t)krow * D;
+    uint16_t* dvr = a.dv + off + (int64_t)krow * D;
+    const float sk = fabsf(a.scale);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int col = db * 32 + 8 * g4 + 4 * hh;
+        u32x2 x, y;
+        x[0] = pack2<DT>(dk[db][4 * g4 + 0] * sk, dk[db][4 * g4 + 1] * sk);
+        x[1] = pack2<DT>(dk[db][4 * g4 + 2] * sk, dk[db][4 * g4 + 3] * sk);
+        y[0] = pack2<DT>(dv[db][4 * g4 + 0], dv[db][4 * g4 + 1]);
+        y[1] = pack2<DT>(dv[db][4 * g4 + 2], dv[db][4 * g4 + 3]);
+        *(u32x2*)(dkr + col) = x;
+        *(u32x2*)(dvr + col) = y;
+      }
+  }
+}
+
+// ---- dQ: one workgroup per 128 queries (query in the lane) ----
+template <int D, int DT, bool CAUSAL>
+__global__ __launch_bounds__(256) void fa_bwd_dq_kernel(const BwdArgs a) {
+  constexpr int NW = 4, NT = 256, BC = 64, KK = D / 16, DB = D / 32, KB = BC / 32;
+  constexpr int CH = BC * D / 8 / NT;
+  using SM = FwdSmem<D, BC>;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SM::STAGE];
+
+  const int nqb = (a.N + 127) / 128;
+  const int bh = blockIdx.x / nqb, qblk0 = blockIdx.x - bh * nqb;
+  if (bh >= a.B * a.H) return;
+  const int qblk = CAUSAL ? nqb - 1 - qblk0 : qblk0;  // longest first
+  const int64_t off = (int64_t)bh * a.N * D;
+  const uint16_t* Qg = a.q + off;
+  const uint16_t* Kg = a.k + off;
+  const uint16_t* Vg = a.v + off;
+  const uint16_t* Gg = a.dout + off;
+  const int N = a.N;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int qw0 = qblk * 128 + w * 32;
+  const int qrow = qw0 + l32;
+
+  u32x4 qf[KK], gf[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const int rr = min(qrow, N - 1);
+    const u32x4 x = *(const u32x4*)(Qg + (int64_t)rr * D + 16 * kk + 8 * hh);
+    const u32x4 y = *(const u32x4*)(Gg + (int64_t)rr * D + 16 * kk + 8 * hh);
+    qf[kk] = (qrow < N ? x : u32x4{0u, 0u, 0u, 0u}) ^ a.qsign;
+    gf[kk] = qrow < N ? y : u32x4{0u, 0u, 0u, 0u};
+  }
+  const float lq = qrow < N ? a.lse[(int64_t)bh * N + qrow] * kLog2e : INFINITY;
+  const float dq_row = qrow < N ? a.dvec[(int64_t)bh * N + qrow] : 0.f;
+
+  f32x16 dqacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dqacc[db][r] = 0.f;
+
+  const int kv_end = CAUSAL ? min(N, (qblk + 1) * 128) : N;
+  const int ntiles = (kv_end + BC - 1) / BC;
+  u32x4 kst[CH], vst[CH];
+  auto fetch = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int ci = tid + NT * c;
+      const int r = ci / (D / 8), col = (ci % (D / 8)) * 8;
+      const int gr = t * BC + r;
+      const int rr = min(gr, N - 1);
+      const u32x4 x = *(const u32x4*)(Kg + (int64_t)rr * D + col);
+      const u32x4 y = *(const u32x4*)(Vg + (int64_t)rr * D + col);
+      kst[c] = gr < kv_end ? x : u32x4{0u, 0u, 0u, 0u};
+      vst[c] = gr < kv_end ? y : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto stash = [&](int buf) __attribute__((always_inline)) {
+    uint16_t* sk = smem + buf * SM::STAGE;
+    uint16_t* sv = sk + SM::KTILE;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int ci = tid + NT * c;
+      const int r = ci / (D / 8), col = (ci % (D / 8)) * 8;
+      *(u32x4*)(sk + r * SM::KSTR + col) = kst[c];
+      *(u32x4*)(sv + r * SM::VSTR + col) = vst[c];
+    }
+  };
+
+  fetch(0);
+  stash(0);
+  const int g16 = lane >> 4, s16 = lane & 15;
+  for (int t = 0; t < ntiles; ++t) {
+    __syncthreads();
+    if (t + 1 < ntiles) fetch(t + 1);
+    const uint16_t* sk = smem + (t & 1) * SM::STAGE;
+    const uint16_t* sv = sk + SM::KTILE;
+    const int key0 = t * BC;
+    // Sᵀ = K Qᵀ and dPᵀ = V dOᵀ: query in the lane, keys in the registers
+    f32x16 s[KB], dp[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
+    }
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const u32x4 ka = *(const u32x4*)(sk + (kb * 32 + l32) * SM::KSTR + 16 * kk + 8 * hh);
+        const u32x4 va = *(const u32x4*)(sv + (kb * 32 + l32) * SM::VSTR + 16 * kk + 8 * hh);
+        s[kb] = mfma32x32x16<DT>(ka, qf[kk], s[kb]);
+        dp[kb] = mfma32x32x16<DT>(va, gf[kk], dp[kb]);
+      }
+    const bool masked = key0 + BC > N || (CAUSAL && key0 + BC - 1 > qw0);
+    u32x4 sf[BC / 16];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        u32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float v2[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int r = 8 * c2 + 2 * e + u;
+            float p = fast_exp2(__builtin_fmaf(s[kb][r], a.c, -lq));
+            if (masked) {
+              const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+              if (key >= N || (CAUSAL && key > qrow)) p = 0.f;
+            }
+            v2[u] = p * (dp[kb][r] - dq_row);
+          }
+          x[e] = pack2<DT>(v2[0], v2[1]);
+        }
+        sf[2 * kb + c2] = x;
+      }
+    // dQᵀ += Kᵀ dSᵀ ; k-slot 8*hh + 4*rd + e of chunk ci is key 16*ci + 8*rd + 4*hh + e
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int ci = 0; ci < BC / 16; ++ci) {
+        const int col = db * 32 + (g16 & 1) * 16 + 4 * (s16 & 3);
+        const int ra = 16 * ci + 4 * hh + (s16 >> 2);
+        const u32x2 lo = lds_read_tr4(sk + ra * SM::KSTR + col);
+        const u32x2 hi = lds_read_tr4(sk + (ra + 8) * SM::KSTR + col);
+        dqacc[db] = mfma32x32x16<DT>(u32x4{lo[0], lo[1], hi[0], hi[1]}, sf[ci], dqacc[db]);
+      }
+    if (t + 1 < ntiles) stash((t + 1) & 1);
+  }
+
+  if (qrow < N) {
+    uint16_t* dqr = a.dq + off + (int64_t)qrow * D;
+    const float sc = a.scale;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        u32x2 x;
+        x[0] = pack2<DT>(dqacc[db][4 * g4 + 0] * sc, dqacc[db][4 * g4 + 1] * sc);
+        x[1] = pack2<DT>(dqacc[db][4 * g4 + 2] * sc, dqacc[db][4 * g4 + 3] * sc);
+        *(u32x2*)(dqr + db * 32 + 8 * g4 + 4 * hh) = x;
+      }
+  }
+}
+
+}  // namespace fa

@@ -21,8 +21,9 @@ EMIN = {"f16": -14, "bf16": -126}
 
 
 def ulp(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Spacing of the 16-bit type at |x| (the subnormal spacing at and near 0)."""
     ax = np.abs(np.asarray(x, dtype=np.float64))
-    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    e = np.where(ax > 0, np.floor(np.log2(np.where(ax > 0, ax, 1.0))), EMIN[dtype])
     e = np.maximum(e, EMIN[dtype])
     return np.exp2(e - MANT[dtype])
 

@@ -154,3 +154,25 @@ def test_fa1_order_argument_errors(L):
     assert L.fa_fwd_fa1_workspace_bytes(1, 2, 0, 64) == 0
     assert L.fa_fwd_fa1_workspace_bytes(1, -2, 64, 64) == -1
     assert L.fa_fwd_fa1_workspace_bytes(1, 2, 64, 80) == -1
+
+
+def test_bwd_argument_errors(L):
+    def call(**kw):
+        a = dict(q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, do=A + 256 * MB, lse=A + 320 * MB,
+                 dq=A + 384 * MB, dk=A + 448 * MB, dv=A + 512 * MB, ws=A + 576 * MB,
+                 B=1, H=2, N=64, d=64, scale=0.125, causal=0, dtype=1)
+        a.update(kw)
+        return L.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["ws"],
+                        a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"], a["dtype"], None)
+    assert call(do=None) == NULL
+    assert call(ws=None) == NULL
+    assert call(dq=A + 384 * MB + 2) == ALIGN
+    assert call(dk=A) == ALIAS            # dk over q
+    assert call(dv=A + 448 * MB) == ALIAS  # dv over dk
+    assert call(ws=A + 320 * MB) == ALIAS  # workspace over lse
+    assert call(d=256) == UNSUP
+    assert call(scale=float("nan")) == SCALE
+    assert call(N=0, q=None) == OK
+    assert L.fa_bwd_workspace_bytes(2, 3, 100, 64) >= 2 * 3 * 100 * 4
+    assert L.fa_bwd_workspace_bytes(2, 3, 0, 64) == 0
+    assert L.fa_bwd_workspace_bytes(2, 3, 100, 70) == -1

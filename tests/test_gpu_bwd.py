@@ -1,0 +1,76 @@
+"""GPU parity of the backward pass (fa_bwd) against the fp64 oracle's
+derivatives, on the same input bits.
+
+Gate: |g - g_ref| <= 8 u S + ulp(g_ref)/2 per element, u being the unit
+roundoff of the 16-bit type (2^-11 fp16, 2^-8 bf16): P and dS enter the
+products rounded to 16 bits and each gradient element sums N such products,
+so its error is a few units of u relative to the gradient's scale
+S = max(max|g_ref|, F). F covers gradients that vanish by cancellation (one
+key: dS = P (dP - D) with dP = D exactly): there the GPU keeps the fp32
+rounding of the two equal terms, at most ~2^-20 d max|dO| max|V| each, times
+d max(|Q|, |K|) |scale| through the last product.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity as P
+import exact_attention_fa2_amd as fa
+from exact_attention_fa2_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+U = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+
+
+def gate_grad(g, ref, dtype, name, floor=0.0):
+    err = np.abs(g - ref)
+    scale = max(np.abs(ref).max(), floor)
+    bound = 8 * U[dtype] * scale + 0.5 * P.ulp(ref, dtype)
+    worst = float((err / np.maximum(scale, 1e-30)).max())
+    assert (err <= bound).all(), f"{name}: max err {err.max():.3e} (rel {worst:.2e}), scale {scale:.3e}"
+    return worst
+
+
+def run(B, H, N, d, dtype, causal, seed, sigma_qk=1.0, scale=None):
+    print(f"[fa_bwd] B{B} H{H} N{N} d{d} {dtype} causal={causal} seed={seed}", flush=True)
+    q, k, v = inputs.make_qkv(B, H, N, d, dtype, seed, sigma_qk)
+    do = inputs.make_like(q, seed + 1000)
+    sc = d ** -0.5 if scale is None else scale
+    qg, kg, vg, dog = (t.cuda() for t in (q, k, v, do))
+    o, lse = fa.attention(qg, kg, vg, causal=causal, scale=sc)
+    dq, dk, dv = fa.attention_backward(qg, kg, vg, o, lse, dog, causal=causal, scale=sc)
+    torch.cuda.synchronize()
+    qd, kd, vd, dod = (P.decode(x, dtype) for x in (q, k, v, do))
+    rq, rk, rv = oracle.attention_bwd(qd, kd, vd, dod, sc, causal)
+    amax = lambda x: float(np.abs(x).max())
+    floor = 2.0 ** -20 * d * amax(dod) * amax(vd) * d * max(amax(qd), amax(kd)) * abs(sc)
+    out = {}
+    for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        out[name] = gate_grad(P.to64(g), r, dtype, name, floor)
+    print("  rel errors", {k2: f"{v2:.2e}" for k2, v2 in out.items()}, flush=True)
+    return out
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,d,dtype", [(1, 64, "f16"), (64, 64, "bf16"), (200, 64, "f16"), (400, 64, "bf16"),
+                                       (129, 128, "f16"), (300, 128, "bf16"), (97, 96, "f16"), (1000, 64, "f16"),
+                                       (700, 128, "bf16")])
+def test_bwd_matches_oracle(N, d, dtype, causal):
+    run(2, 2, N, d, dtype, causal, seed=N + d)
+
+
+def test_bwd_scale_variants():
+    run(1, 2, 150, 64, "f16", False, seed=7, scale=-0.1)
+    run(1, 2, 150, 64, "bf16", True, seed=8, scale=0.3, sigma_qk=2.0)
+
+
+def test_bwd_deterministic():
+    q, k, v = (t.cuda() for t in inputs.make_qkv(1, 4, 500, 64, "bf16", 9))
+    do = inputs.make_like(q.cpu(), 10).cuda()
+    o, lse = fa.attention(q, k, v, causal=True)
+    g1 = fa.attention_backward(q, k, v, o, lse, do, causal=True)
+    g2 = fa.attention_backward(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(g1, g2))
