@@ -7,7 +7,10 @@ Inputs are resident in HBM before timing; R rotating input sets (>= 512 MB
 in total) keep the 256 MB Infinity Cache from serving them between steps.
 The K timed launches are captured once in a HIP graph and replayed, so the
 host's launch overhead cannot starve the GPU; HIP events recorded on the
-launch stream give the average kernel duration used for the roofline.
+launch stream give the average kernel duration used for the roofline. After
+the W warmup steps, untimed replays run for --settle seconds: kernel times
+keep falling for tens of milliseconds after a burst starts (clocks, address
+translation), and the timed steps should see the steady state.
 
 Prints ONE JSON line on stdout (details go to stderr).
 """
@@ -90,16 +93,78 @@ def cpu_baseline(w: inputs.Workload, budget_s: float):
     }
 
 
+def bench_varlen(args, torch, fa, dev) -> int:
+    """Packed variable-length batch through fa_fwd_varlen (same timing scheme)."""
+    vm = inputs.VARLEN_MIX
+    seqlens, H, d = vm["seqlens"], vm["H"], vm["d"]
+    T = sum(seqlens)
+    aflops = sum(acc.alg_flops(1, H, n, d, vm["causal"]) for n in seqlens)
+    abytes = acc.alg_bytes(1, H, T, d)
+    R = max(1, math.ceil(ROTATE_BYTES / abytes))
+    sets = []
+    for r in range(R):
+        q, k, v, cu = inputs.make_varlen(seqlens, H, d, vm["dtype"], seed=r)
+        q, k, v, cu = (t.to(dev) for t in (q, k, v, cu))
+        sets.append((q, k, v, cu, torch.empty_like(q), torch.empty((H, T), dtype=torch.float32, device=dev)))
+    scale = d ** -0.5
+    stream = torch.cuda.Stream()
+
+    def launch(i):
+        q, k, v, cu, o, lse = sets[i % R]
+        fa.fa_fwd_varlen(q, k, v, o, lse, cu, len(seqlens), T, max(seqlens), H, d, scale, vm["causal"])
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            launch(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(K):
+            launch(i)
+    torch.cuda.synchronize()
+    t_set = time.perf_counter()
+    while time.perf_counter() - t_set < args.settle:
+        graph.replay()
+        torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        graph.replay()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_s = ev0.elapsed_time(ev1) * 1e-3 / K
+    log(f"varlen_mix: {len(seqlens)} sequences {sorted(set(seqlens))}, T={T}, H={H}, d={d}: kernel avg "
+        f"{kern_s*1e6:.2f} us; {aflops/kern_s/1e12:.1f} TFLOP/s alg")
+    print(json.dumps({
+        "metric": "attn fwd TFLOP/s, packed variable-length batch", "value": round(aflops / (wall / K) / 1e12, 3),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / K, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": vm["dtype"], "data": "synthetic",
+        "config": {"workload": "varlen_mix", "seqlens": seqlens, "H": H, "d": d, "input_sets": R},
+        "roofline": {"bound": "mfma", "achieved": round(aflops / kern_s / 1e12, 2),
+                     "peak": acc.MFMA_PEAK_TFLOPS_16BIT, "unit": "TFLOP/s",
+                     "frac": round(aflops / kern_s / 1e12 / acc.MFMA_PEAK_TFLOPS_16BIT, 4), "traffic": None,
+                     "kernel": "fa_fwd_varlen", "kernel_us": round(kern_s * 1e6, 3)}}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(inputs.WORKLOADS))
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(inputs.WORKLOADS) + ["varlen_mix"])
+    ap.add_argument("--layout", default="bhnd", choices=["bhnd", "bnhd", "qkvpacked"],
+                    help="tensor layout at the boundary (fa_fwd / fa_fwd_strided)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--eager", action="store_true", help="launch from Python each step (no graph)")
     ap.add_argument("--warm-cache", action="store_true", help="one input set (cache-resident)")
+    ap.add_argument("--settle", type=float, default=0.5,
+                    help="seconds of untimed steps after the warmup, so that clocks and address "
+                         "translation reach steady state before the timed steps")
     ap.add_argument("--impl", default="fa2", choices=["fa2", "fa1_order", "bwd"],
                     help="fa2: fa_fwd (default); fa1_order: the FlashAttention-1 loop-order "
                          "ablation; bwd: fa_bwd (the backward by recomputation)")
@@ -128,6 +193,8 @@ def main() -> int:
         log(f"copied {n} bytes x3")
         return 0
 
+    if args.workload == "varlen_mix":
+        return bench_varlen(args, torch, fa, dev)
     w = inputs.WORKLOADS[args.workload]
     elem = 2
     abytes = acc.alg_bytes(w.B, w.H, w.N, w.d, elem)
@@ -147,7 +214,13 @@ def main() -> int:
     sets = []
     for r in range(R):
         q, k, v = (t.to(dev) for t in inputs.make_workload(w, seed=r))
-        o = torch.empty_like(q)
+        if args.layout == "bnhd":
+            q, k, v = (t.transpose(1, 2).contiguous() for t in (q, k, v))
+        elif args.layout == "qkvpacked":
+            qkv = torch.stack([t.transpose(1, 2) for t in (q, k, v)], dim=2).contiguous()
+            q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+        o = torch.empty_like(q) if args.layout == "bhnd" else torch.empty(
+            (w.B, w.N, w.H, w.d), dtype=q.dtype, device=dev)
         lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
         sets.append((q, k, v, o, lse))
     stream = torch.cuda.Stream()
@@ -165,7 +238,11 @@ def main() -> int:
 
     def launch(i):
         q, k, v, o, lse = sets[i % R]
-        if args.impl == "fa2":
+        if args.impl == "fa2" and args.layout != "bhnd":
+            st = fa._strides_bnhd
+            fa.fa_fwd_strided(q, k, v, o, lse, w.B, w.H, w.N, w.d, w.scale, w.causal,
+                              st(q), st(k), st(v), st(o))
+        elif args.impl == "fa2":
             fa.fa_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.d, w.scale, w.causal)
         elif args.impl == "fa1_order":
             fa.fa_fwd_fa1_order(q, k, v, o, lse, ws, w.B, w.H, w.N, w.d, w.scale, w.causal)
@@ -193,6 +270,17 @@ def main() -> int:
         if not torch.equal(out_idx, ref_o):
             log("graph replay disagrees with the eager launch")
             return 1
+
+    # untimed settle phase: the same steps until `settle` seconds have passed
+    t_set = time.perf_counter()
+    with torch.cuda.stream(stream):
+        while time.perf_counter() - t_set < args.settle:
+            if graph is not None:
+                graph.replay()
+            else:
+                for i in range(K):
+                    launch(i)
+            torch.cuda.synchronize()
 
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -235,7 +323,8 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
-                   "input_sets": R, "graph": graph is not None, "impl": args.impl,
+                   "input_sets": R, "graph": graph is not None, "impl": args.impl, "layout": args.layout,
+                   "settle_s": args.settle,
                    "parallelism": "none (1 GPU)"},
         "roofline": {
             "bound": bound,

@@ -281,17 +281,43 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
   stash(0);
 
 
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();
-    if (t + 1 < ntiles) fetch(t + 1);
-    const int key0 = t * BC;
-    const uint16_t* sk = smem + (t & 1) * SM::STAGE;
-    const uint16_t* sv = sk + SM::KTILE;
-    // ragged last tile, or (causal) keys after some query of this wave
-    const bool need_mask = (key0 + BC > Nb) || (CAUSAL && key0 + BC - 1 > qw0);
-    tile_step_fwd<D, DT, CAUSAL, QB, BC, SM::KSTR, SM::VSTR>(need_mask, sk, sv, key0, Nb, qw0, lane,
-                                                             a.c, qf, oacc, m_run, l_run);
-    if (t + 1 < ntiles) stash((t + 1) & 1);
+  // A ragged last tile that fits in 32 keys runs as a half-width step after
+  // the main loop. Waves whose rows all lie past the end run a loop that only
+  // helps with the loads (same barriers). Keeping each loop body a single
+  // path lets the output accumulator stay in place across iterations.
+  const bool tail32 = BC == 64 && kv_end - (ntiles - 1) * BC <= 32;
+  const int nmain = tail32 ? ntiles - 1 : ntiles;
+  if (qw0 < Nb) {
+    for (int t = 0; t < nmain; ++t) {
+      __syncthreads();
+      if (t + 1 < ntiles) fetch(t + 1);
+      const int key0 = t * BC;
+      const uint16_t* sk = smem + (t & 1) * SM::STAGE;
+      const uint16_t* sv = sk + SM::KTILE;
+      // ragged last tile, or (causal) keys after some query of this wave
+      const bool need_mask = (key0 + BC > Nb) || (CAUSAL && key0 + BC - 1 > qw0);
+      tile_step_fwd<D, DT, CAUSAL, QB, BC, SM::KSTR, SM::VSTR>(need_mask, sk, sv, key0, Nb, qw0, lane,
+                                                               a.c, qf, oacc, m_run, l_run);
+      if (t + 1 < ntiles) stash((t + 1) & 1);
+    }
+    if constexpr (BC == 64) {
+      if (tail32) {
+        const int t = ntiles - 1;
+        __syncthreads();
+        const uint16_t* sk = smem + (t & 1) * SM::STAGE;
+        tile_step_fwd<D, DT, CAUSAL, QB, 32, SM::KSTR, SM::VSTR>(true, sk, sk + SM::KTILE, t * BC, Nb, qw0,
+                                                                 lane, a.c, qf, oacc, m_run, l_run);
+      }
+    }
+  } else {
+    for (int t = 0; t < ntiles; ++t) {
+      __syncthreads();
+      if (t + 1 < ntiles) {
+        fetch(t + 1);
+        stash((t + 1) & 1);
+      }
+    }
+    return;
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----

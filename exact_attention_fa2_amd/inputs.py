@@ -56,6 +56,12 @@ WORKLOADS = {
 }
 
 
+# A packed batch of feature maps of four sizes (10x10, 20x20, 40x40, 80x80),
+# four of each, for the variable-length entry point.
+VARLEN_MIX = {"name": "varlen_mix", "seqlens": [100, 400, 1600, 6400] * 4, "H": 4, "d": 64,
+              "dtype": "f16", "causal": False}
+
+
 def make_qkv(B: int, H: int, N: int, d: int, dtype: str, seed: int,
              sigma_qk: float = 1.0, sigma_v: float = 1.0):
     """Seeded Q, K, V as contiguous CPU tensors [B, H, N, d] of ``dtype``."""
