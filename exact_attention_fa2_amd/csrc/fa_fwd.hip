@@ -9,10 +9,20 @@
 namespace fa {
 namespace {
 
+// Rows per workgroup: as many blocks as NW*32*QB rows need, then the rows
+// spread evenly over them in 32-row units (N = 400 on 256-row workgroups:
+// 224 + 176 rows instead of 256 + 144), so no block waits on a fuller one.
+inline int even_rows(int N, int br_max) {
+  const int nqb = (N + br_max - 1) / br_max;
+  const int units = (N + 31) / 32;
+  return 32 * ((units + nqb - 1) / nqb);
+}
+
 template <int D, int DT, bool CAUSAL, int NW, int QB, int BC>
 int launch_one(FwdArgs a, hipStream_t st) {
   constexpr int BR = NW * 32 * QB;
-  a.nqb = (a.N + BR - 1) / BR;
+  a.br = even_rows(a.N, BR);
+  a.nqb = (a.N + a.br - 1) / a.br;
   const int64_t total = (int64_t)a.B * a.H * a.nqb;
   if (total > (INT64_C(1) << 30)) return FA_ERR_DIM;
   a.total = (int)total;
@@ -25,6 +35,7 @@ int launch_one(FwdArgs a, hipStream_t st) {
 template <int D, int DT, bool CAUSAL, int NW, int QB, int BC>
 int launch_pipe(FwdArgs a, hipStream_t st) {
   constexpr int BR = NW * 32 * QB;
+  a.br = BR;
   a.nqb = (a.N + BR - 1) / BR;
   const int64_t total = (int64_t)a.B * a.H * a.nqb;
   if (total > (INT64_C(1) << 30)) return FA_ERR_DIM;

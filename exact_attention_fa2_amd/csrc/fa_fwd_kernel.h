@@ -50,6 +50,8 @@ struct FwdArgs {
   const int32_t* cu_seqlens; // null: every sequence has N rows
   int B, H, N;               // N: rows per sequence (an upper bound with cu_seqlens)
   int nqb;                   // query blocks per (batch, head)
+  int br;                    // query rows per workgroup (a multiple of 32 rows per wave,
+                             // at most NW*32*QB; set so that the blocks of a head are even)
   int total;                 // B * H * nqb
   float c;                   // max(|scale| * log2(e), 1e-30): strictly positive
   uint32_t qsign;            // 0x80008000 when scale < 0, else 0
@@ -206,7 +208,8 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
     row0 = a.cu_seqlens[b];
     Nb = a.cu_seqlens[b + 1] - (int)row0;
   }
-  if (qblk * BR >= Nb) return;  // uniform over the workgroup
+  const int br = a.br;          // rows of this workgroup (<= BR)
+  if (qblk * br >= Nb) return;  // uniform over the workgroup
 
   const uint16_t* Qg = a.q + b * a.q_sb + h * a.q_sh + row0 * a.q_sr;
   const uint16_t* Kg = a.k + b * a.k_sb + h * a.k_sh + row0 * a.k_sr;
@@ -217,7 +220,8 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int qw0 = qblk * BR + w * QW;  // first query row of this wave
+  const int qw0 = qblk * br + w * QW;  // first query row of this wave
+  const bool wave_rows = w * QW < br;   // waves beyond br only help with the loads
 
   // ---- Q fragments (B operand of Sᵀ = K Qᵀ), kept in registers ----
   u32x4 qf[QB][KK];
@@ -232,7 +236,7 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
     }
   }
 
-  const int kv_end = CAUSAL ? min(Nb, (qblk + 1) * BR) : Nb;
+  const int kv_end = CAUSAL ? min(Nb, (qblk + 1) * br) : Nb;
   const int ntiles = (kv_end + BC - 1) / BC;
 
   // ---- global -> register staging of one K/V tile ----
@@ -287,7 +291,7 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
   // path lets the output accumulator stay in place across iterations.
   const bool tail32 = BC == 64 && kv_end - (ntiles - 1) * BC <= 32;
   const int nmain = tail32 ? ntiles - 1 : ntiles;
-  if (qw0 < Nb) {
+  if (wave_rows && qw0 < Nb) {
     for (int t = 0; t < nmain; ++t) {
       __syncthreads();
       if (t + 1 < ntiles) fetch(t + 1);
@@ -327,7 +331,7 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
     const float l_lse = DT == DT_F16 ? l_tot : l_run[1][j] + xor_lane32(l_run[1][j]);
     const float inv = 1.f / l_tot;
     const int qrow = qw0 + 32 * j + l32;
-    if (qrow < Nb) {
+    if (qrow < Nb && wave_rows) {
       uint16_t* orow = Og + qrow * a.o_sr;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
