@@ -152,6 +152,7 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
   const int64_t st[12] = {q_sb, q_sh, q_sr, k_sb, k_sh, k_sr, v_sb, v_sh, v_sr, o_sb, o_sh, o_sr};
   for (int i = 0; i < 12; ++i) {
     if (st[i] < 0) return FA_ERR_DIM;
+    if (i % 3 == 2 && st[i] > kMaxRowStride) return FA_ERR_DIM;
     if (st[i] % 8) return FA_ERR_ALIGN;
   }
   // the largest element offset reached must stay addressable
@@ -200,6 +201,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
   if (B < 0) return FA_ERR_DIM;
   if (B == 0 || elems == 0 || max_seqlen == 0) return FA_OK;
   if (max_seqlen > T) return FA_ERR_DIM;
+  if ((int64_t)H * d > kMaxRowStride) return FA_ERR_DIM;
   if (!q || !k || !v || !o || !lse || !cu_seqlens) return FA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       (reinterpret_cast<uintptr_t>(lse) & 3) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3))

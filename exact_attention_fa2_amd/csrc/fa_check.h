@@ -7,6 +7,9 @@
 #include "fa_fwd_kernel.h"
 
 namespace fa {
+// Largest row stride (elements) of any tensor: the kernels address a tile of
+// up to 64 rows with 32-bit byte offsets.
+constexpr int64_t kMaxRowStride = INT64_C(1) << 24;
 bool mul_ok(int64_t a, int64_t b, int64_t* out);
 bool head_dim_ok(int d);
 bool aligned16(const void* p);

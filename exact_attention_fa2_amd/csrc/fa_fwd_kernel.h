@@ -22,12 +22,17 @@
 //    with ds_read_b64_tr_b16, the gfx950 LDS transpose read.
 //  * Softmax runs in the log2 domain: c = |scale|*log2(e), p = exp2(s*c - m).
 //    A negative scale is folded into Q by flipping its sign bits (exact).
-//  * The running max is only raised when it grows by more than kRescaleGap
-//    (log2 units): partial sums then stay below 2^kRescaleGap and the costly
-//    rescale of the output accumulator is skipped on most tiles. The final
-//    O = acc / l and LSE = (m + log2 l) ln 2 are exact for any stale m.
-//  * K/V for tile t+1 are fetched into registers while tile t is computed
-//    from the other half of a double-buffered LDS, one barrier per tile.
+//  * The reference m of a row is its first tile's max. Later tiles skip the
+//    max entirely: their weights p = exp2(s*c - m) are formed with the
+//    standing m and only their partial sums are checked; a tile whose
+//    partial sums reach kPartialCap (so some weight could leave the 16-bit
+//    range) is redone with the true max and a rescale of the output
+//    accumulator. O = acc / l and LSE = (m + log2 l) ln 2 are exact for any
+//    reference m, so only the range of p matters, not which m is used.
+//  * K/V for tile t+1 are fetched into registers (buffer loads whose
+//    descriptor covers only the tile's valid rows: rows past the end read
+//    as zero with no per-lane test) while tile t is computed from the other
+//    half of a double-buffered LDS, one barrier per tile.
 //  * Workgroup ids are remapped so that each XCD (workgroups are dealt
 //    round-robin over the 8 XCDs) walks whole heads, sharing K/V in its L2;
 //    causal blocks run longest first.
@@ -57,7 +62,14 @@ struct FwdArgs {
   uint32_t qsign;            // 0x80008000 when scale < 0, else 0
 };
 
-constexpr float kRescaleGap = 8.0f;
+// A weight tile is accepted when each lane's partial sums of its 16-bit
+// weights (at most 8 weights each) stay below this: every weight is then below
+// 2^15, inside the fp16 range, and the fp32 sums cannot overflow.
+constexpr float kPartialCap = 32768.0f;
+
+// dword 3 of a raw buffer descriptor on gfx950 (32-bit data format, raw
+// addressing; loads past num_records return zero)
+constexpr int kBufferDword3 = 0x00020000;
 
 template <int D, int BC>
 struct FwdSmem {
@@ -70,9 +82,10 @@ struct FwdSmem {
 };
 
 // One K/V tile for one wave: Sᵀ = K Qᵀ, online-softmax update, Oᵀ += Vᵀ Pᵀ.
-// Masked tiles (wave-uniform flag) apply the ragged-tail and causal masks.
+// Masked tiles (wave-uniform flag) apply the ragged-tail and causal masks;
+// `first` (wave-uniform) marks the first tile of the wave's rows.
 template <int D, int DT, bool CAUSAL, int QB, int BC, int KSTR, int VSTR>
-__device__ __forceinline__ void tile_step_fwd(bool masked, const uint16_t* __restrict__ sk,
+__device__ __forceinline__ void tile_step_fwd(bool first, bool masked, const uint16_t* __restrict__ sk,
                                                const uint16_t* __restrict__ sv, int key0, int Nb,
                                                int qw0, int lane, float c, const u32x4 (&qf)[QB][D / 16],
                                                f32x16 (&oacc)[QB][D / 32], float (&m_run)[QB],
@@ -80,51 +93,102 @@ __device__ __forceinline__ void tile_step_fwd(bool masked, const uint16_t* __res
   constexpr int KK = D / 16, DB = D / 32, KB = BC / 32;
   const int l32 = lane & 31, hh = lane >> 5;
 
-  // Sᵀ = K_t Qᵀ : s[kb][j] covers keys kb*32.. and queries 32j..
+  // Sᵀ = K_t Qᵀ : s[kb][j] covers keys kb*32.. and queries 32j.. (a redone
+  // tile computes it again from LDS rather than keeping it live)
   f32x16 s[KB][QB];
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-    for (int j = 0; j < QB; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][j][r] = 0.f;
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const u32x4 ka = *(const u32x4*)(sk + (kb * 32 + l32) * KSTR + 16 * kk + 8 * hh);
-#pragma unroll
-      for (int j = 0; j < QB; ++j) s[kb][j] = mfma32x32x16<DT>(ka, qf[j][kk], s[kb][j]);
-    }
-  }
-
-  if (masked) {
+  auto scores = [&](int z) __attribute__((always_inline)) {
+    const uint16_t* kt = sk + z;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int j = 0; j < QB; ++j) {
-        const int qrow = qw0 + 32 * j + l32;
+      for (int j = 0; j < QB; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const bool dead = key >= Nb || (CAUSAL && key > qrow);
-          if (dead) s[kb][j][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r) s[kb][j][r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const u32x4 ka = *(const u32x4*)(kt + (kb * 32 + l32) * KSTR + 16 * kk + 8 * hh);
+#pragma unroll
+        for (int j = 0; j < QB; ++j) s[kb][j] = mfma32x32x16<DT>(ka, qf[j][kk], s[kb][j]);
       }
-  }
+    }
+    if (masked) {
+      // register r of block kb holds key key0 + 4*hh + off, off = 32*kb +
+      // 8*(r/4) + r%4; it is dead when past the end (key >= Nb) or, causal,
+      // after the query (key > qrow): off > lim with one per-lane limit
+#pragma unroll
+      for (int j = 0; j < QB; ++j) {
+        const int base = key0 + 4 * hh - z;
+        int lim = Nb - 1 - base;
+        if constexpr (CAUSAL) lim = min(lim, qw0 + 32 * j + l32 - base);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[kb][j][r] = -INFINITY;
+      }
+    }
+  };
+  scores(0);
 
   // online softmax (log2 domain)
   u32x4 pf[QB][BC / 16];
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
-    float mx = -INFINITY;
+    // weights p = exp2(s*c - mref) packed to 16 bits; lp: 4 partial sums of
+    // the 16-bit weights (the ones that multiply V, so O is normalised by
+    // exactly what it accumulates); lf: fp32 sums for the bf16 LSE
+    float lp[4], lf[4];
+    auto probs = [&](float mref) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+      for (int e = 0; e < 4; ++e) lp[e] = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][j][r]);
-    mx = fmaxf(mx, xor_lane32(mx));
-    const float m_new = fmaxf(m_run[j], mx * c);
-    if (wave_any(m_new > m_run[j] + kRescaleGap)) {
+      for (int kb = 0; kb < KB; ++kb) {
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          // c > 0 always (clamped on the host), so a masked -inf stays -inf
+          p[r] = fast_exp2(__builtin_fmaf(s[kb][j][r], c, -mref));
+          if constexpr (DT == DT_BF16) {
+            if (kb == 0 && r < 4) lf[r] = p[r];
+            else lf[r & 3] += p[r];
+          }
+        }
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          u32x4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[e] = pack2<DT>(p[8 * c2 + 2 * e], p[8 * c2 + 2 * e + 1]);
+            lp[e] = dot2_sum<DT>(x[e], lp[e]);
+          }
+          pf[j][2 * kb + c2] = x;
+        }
+      }
+    };
+    auto tile_max = [&]() __attribute__((always_inline)) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][j][r]);
+      return fmaxf(mx, xor_lane32(mx)) * c;
+    };
+    // the first tile of a row sets its reference max (the accumulator is
+    // still zero, so nothing needs rescaling)
+    if (first) m_run[j] = tile_max();
+    probs(m_run[j] == -INFINITY ? 0.f : m_run[j]);
+    const float pk = fmaxf(fmaxf(lp[0], lp[1]), fmaxf(lp[2], lp[3]));
+    if (wave_any(!(pk < kPartialCap))) {
+      // some weight may have left the 16-bit range: raise the reference to
+      // the true max, rescale what has been accumulated, redo the weights
+      // (through an offset the compiler cannot see is zero, so that K and
+      // the mask are formed again rather than kept live across the fast path)
+      int zero = 0;
+      asm volatile("" : "+s"(zero));
+      scores(zero);
+      const float m_new = fmaxf(m_run[j], tile_max());
       const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[j] - m_new);
       l_run[0][j] *= alpha;
       l_run[1][j] *= alpha;
@@ -133,30 +197,7 @@ __device__ __forceinline__ void tile_step_fwd(bool masked, const uint16_t* __res
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[j][db][r] *= alpha;
       m_run[j] = m_new;
-    }
-    const float mref = (m_run[j] == -INFINITY) ? 0.f : m_run[j];
-    // l[0]: sum of the 16-bit weights that multiply V (normalises O exactly
-    // like the product it divides); l[1]: fp32 sum for the bf16 LSE
-    float lp[4] = {0.f, 0.f, 0.f, 0.f}, lf[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      float p[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        // c > 0 always (clamped on the host), so a masked -inf stays -inf
-        p[r] = fast_exp2(__builtin_fmaf(s[kb][j][r], c, -mref));
-        if constexpr (DT == DT_BF16) lf[r & 3] += p[r];
-      }
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        u32x4 x;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[e] = pack2<DT>(p[8 * c2 + 2 * e], p[8 * c2 + 2 * e + 1]);
-          lp[e] = dot2_sum<DT>(x[e], lp[e]);
-        }
-        pf[j][2 * kb + c2] = x;
-      }
+      probs(m_new == -INFINITY ? 0.f : m_new);
     }
     l_run[0][j] += (lp[0] + lp[1]) + (lp[2] + lp[3]);
     if constexpr (DT == DT_BF16) l_run[1][j] += (lf[0] + lf[1]) + (lf[2] + lf[3]);
@@ -240,21 +281,30 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
   const int ntiles = (kv_end + BC - 1) / BC;
 
   // ---- global -> register staging of one K/V tile ----
+  // Per tile, a buffer descriptor based at the tile's first row whose size
+  // ends with the last valid row (host guarantee: BC row strides < 2^31
+  // bytes); each lane's byte offset inside the tile is fixed.
   u32x4 kst[CH], vst[CH];
-  auto fetch = [&](int t) {
-    const int base = t * BC;
+  uint32_t koff[CH], voff[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int ci = tid + NT * c;
+    const int r = ci / (D / 8), col = (ci % (D / 8)) * 8;
+    koff[c] = (uint32_t)(r * (a.k_sr * 2) + col * 2);
+    voff[c] = (uint32_t)(r * (a.v_sr * 2) + col * 2);
+  }
+  auto fetch = [&](int t) __attribute__((always_inline)) {
+    const int rows = min(kv_end - t * BC, BC);  // >= 1
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Kg + (int64_t)t * BC * a.k_sr), (short)0, (int)((rows - 1) * (a.k_sr * 2) + D * 2),
+        kBufferDword3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Vg + (int64_t)t * BC * a.v_sr), (short)0, (int)((rows - 1) * (a.v_sr * 2) + D * 2),
+        kBufferDword3);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int ci = tid + NT * c;
-      const int r = ci / (D / 8), col = (ci % (D / 8)) * 8;
-      const int gr = base + r;
-      u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
-      if (gr < kv_end) {
-        xk = *(const u32x4*)(Kg + gr * a.k_sr + col);
-        xv = *(const u32x4*)(Vg + gr * a.v_sr + col);
-      }
-      kst[c] = xk;
-      vst[c] = xv;
+      kst[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff[c], 0, 0));
+      vst[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff[c], 0, 0));
     }
   };
   auto stash = [&](int buf) {
@@ -300,8 +350,8 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
       const uint16_t* sv = sk + SM::KTILE;
       // ragged last tile, or (causal) keys after some query of this wave
       const bool need_mask = (key0 + BC > Nb) || (CAUSAL && key0 + BC - 1 > qw0);
-      tile_step_fwd<D, DT, CAUSAL, QB, BC, SM::KSTR, SM::VSTR>(need_mask, sk, sv, key0, Nb, qw0, lane,
-                                                               a.c, qf, oacc, m_run, l_run);
+      tile_step_fwd<D, DT, CAUSAL, QB, BC, SM::KSTR, SM::VSTR>(t == 0, need_mask, sk, sv, key0, Nb, qw0,
+                                                               lane, a.c, qf, oacc, m_run, l_run);
       if (t + 1 < ntiles) stash((t + 1) & 1);
     }
     if constexpr (BC == 64) {
@@ -309,8 +359,8 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
         const int t = ntiles - 1;
         __syncthreads();
         const uint16_t* sk = smem + (t & 1) * SM::STAGE;
-        tile_step_fwd<D, DT, CAUSAL, QB, 32, SM::KSTR, SM::VSTR>(true, sk, sk + SM::KTILE, t * BC, Nb, qw0,
-                                                                 lane, a.c, qf, oacc, m_run, l_run);
+        tile_step_fwd<D, DT, CAUSAL, QB, 32, SM::KSTR, SM::VSTR>(t == 0, true, sk, sk + SM::KTILE, t * BC,
+                                                                 Nb, qw0, lane, a.c, qf, oacc, m_run, l_run);
       }
     }
   } else {

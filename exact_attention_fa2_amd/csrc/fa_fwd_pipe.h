@@ -23,7 +23,7 @@
 
 namespace fa {
 
-constexpr uint32_t kBufferDword3 = 0x00020000u;  // gfx9-family raw buffer descriptor word 3
+constexpr float kRescaleGap = 8.0f;  // raise the running max only when it grows by more than this (log2)
 
 // XOR swizzle of the 16-byte chunk slot of row r. LDS has 64 banks; a 16-byte
 // read is served 16 lanes at a time and an 8-byte transposing read 32 lanes

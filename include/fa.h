@@ -86,7 +86,8 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
  *
  *   *_sb, *_sh, *_sr : strides in ELEMENTS of the batch, head and row axes of
  *                      q, k, v and o; the head-dim axis is contiguous. Row
- *                      and head strides must be multiples of 8 elements.
+ *                      and head strides must be multiples of 8 elements;
+ *                      row strides at most 2^24 elements (FA_ERR_DIM beyond).
  *   lse     : [B, H, N] fp32 contiguous.
  * Overlap of o with q/k/v is only checked for identical base pointers.
  */
@@ -111,6 +112,7 @@ int fa_fwd_strided(const void *q, const void *k, const void *v, void *o, float *
  *   max_seqlen : an upper bound of cu[b+1]-cu[b] over b (sizes the grid).
  *   lse        : [H, T] fp32.
  * Attention never crosses sequence boundaries; causal is per sequence.
+ * H*d (the row stride) must be at most 2^24 (FA_ERR_DIM beyond).
  */
 int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
                   const int32_t *cu_seqlens, int B, int T, int max_seqlen, int H, int d,

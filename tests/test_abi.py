@@ -107,6 +107,10 @@ def test_strided_argument_errors(L):
     bad = list(s)
     bad[0] = 1 << 62  # far element out of the addressable range
     assert strided(L, bad) == DIM
+    for i in (2, 5, 8, 11):  # a row stride past 2^24 elements (32-bit tile offsets)
+        bad = list(s)
+        bad[i] = (1 << 24) + 8
+        assert strided(L, bad) == DIM
     assert strided(L, o=A) == ALIAS
     assert strided(L, v=None) == NULL
     assert strided(L, d=32) == UNSUP
@@ -123,6 +127,7 @@ def test_varlen_argument_errors(L):
     assert call(maxs=-1) == DIM
     assert call(maxs=301) == DIM
     assert call(T=-3) == DIM
+    assert call(H=(1 << 24) // 64 + 1) == DIM  # row stride H*d past 2^24
     assert call(B=-1) == DIM
     assert call(B=0) == OK
     assert call(cu=A + 300 * MB + 2) == ALIGN
