@@ -71,6 +71,21 @@ constexpr float kPartialCap = 32768.0f;
 // addressing; loads past num_records return zero)
 constexpr int kBufferDword3 = 0x00020000;
 
+// XOR swizzle of the 16-byte chunk slot of row r. LDS has 64 banks; a 16-byte
+// read is served 16 lanes at a time and an 8-byte transposing read 32 lanes
+// at a time, so the slot must (a) differ over 16 consecutive rows read at
+// the same chunk (K operand) and (b) spread 4 aligned rows x 4 aligned
+// chunks over 16 distinct bank groups (V operand). With 256-byte rows (d=128)
+// the bank group is the slot itself; with 128-byte rows (d=64) it is the
+// slot plus 8 for odd rows.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128)
+    return 4 * (r & 3) + ((r >> 2) & 3);
+  else
+    return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+
 template <int D, int BC>
 struct FwdSmem {
   static constexpr int KSTR = D + 8;   // padded K row (halves): conflict-free 16-byte reads
@@ -80,6 +95,17 @@ struct FwdSmem {
   static constexpr int STAGE = KTILE + VTILE;
   static constexpr int BYTES = 2 * STAGE * 2;
 };
+
+// Offsets (halves) into an LDS K or V tile: rows padded to STR halves, or,
+// with STR == 0, unpadded rows of D halves whose 16-byte chunks are XOR
+// swizzled by swz<D> (the layout the LDS-DMA loads write).
+template <int D, int STR>
+__device__ __forceinline__ int lds_off(int row, int col) {
+  if constexpr (STR != 0)
+    return row * STR + col;
+  else
+    return row * D + ((((col >> 3) ^ swz<D>(row))) << 3) + (col & 7);
+}
 
 // One K/V tile for one wave: Sᵀ = K Qᵀ, online-softmax update, Oᵀ += Vᵀ Pᵀ.
 // Masked tiles (wave-uniform flag) apply the ragged-tail and causal masks;
@@ -108,7 +134,7 @@ __device__ __forceinline__ void tile_step_fwd(bool first, bool masked, const uin
     for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const u32x4 ka = *(const u32x4*)(kt + (kb * 32 + l32) * KSTR + 16 * kk + 8 * hh);
+        const u32x4 ka = *(const u32x4*)(kt + lds_off<D, KSTR>(kb * 32 + l32, 16 * kk + 8 * hh));
 #pragma unroll
         for (int j = 0; j < QB; ++j) s[kb][j] = mfma32x32x16<DT>(ka, qf[j][kk], s[kb][j]);
       }
@@ -211,8 +237,8 @@ __device__ __forceinline__ void tile_step_fwd(bool first, bool masked, const uin
     for (int ci = 0; ci < BC / 16; ++ci) {
       const int col = db * 32 + (g & 1) * 16 + 4 * (s16 & 3);
       const int rowa = 16 * ci + 4 * hh + (s16 >> 2);
-      const u32x2 lo = lds_read_tr4(sv + rowa * VSTR + col);
-      const u32x2 hi = lds_read_tr4(sv + (rowa + 8) * VSTR + col);
+      const u32x2 lo = lds_read_tr4(sv + lds_off<D, VSTR>(rowa, col));
+      const u32x2 hi = lds_read_tr4(sv + lds_off<D, VSTR>(rowa + 8, col));
       const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
       for (int j = 0; j < QB; ++j) oacc[j][db] = mfma32x32x16<DT>(va, pf[j][ci], oacc[j][db]);
@@ -335,14 +361,21 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
   stash(0);
 
 
-  // A ragged last tile that fits in 32 keys runs as a half-width step after
-  // the main loop. Waves whose rows all lie past the end run a loop that only
-  // helps with the loads (same barriers). Keeping each loop body a single
-  // path lets the output accumulator stay in place across iterations.
-  const bool tail32 = BC == 64 && kv_end - (ntiles - 1) * BC <= 32;
-  const int nmain = tail32 ? ntiles - 1 : ntiles;
+  // The tiles a wave computes end with the last key any of its rows sees
+  // (causal: its own diagonal; tiles past that are fully masked and are
+  // skipped). A ragged last tile that fits in 32 keys -- the ragged end of
+  // a sequence, or a causal diagonal block of a wave whose rows start on a
+  // 64-key boundary -- runs as a half-width step. After its last tile a wave
+  // keeps helping with the loads until the workgroup's last tile (same
+  // barriers), and waves with no rows only help with the loads. Keeping each
+  // loop body a single path lets the output accumulator stay in place.
   if (wave_rows && qw0 < Nb) {
-    for (int t = 0; t < nmain; ++t) {
+    const int wave_end = CAUSAL ? min(kv_end, qw0 + QW) : kv_end;
+    const int wnt = (wave_end + BC - 1) / BC;
+    const bool tail32 = BC == 64 && wave_end - (wnt - 1) * BC <= 32;
+    const int nmain = tail32 ? wnt - 1 : wnt;
+    int t = 0;
+    for (; t < nmain; ++t) {
       __syncthreads();
       if (t + 1 < ntiles) fetch(t + 1);
       const int key0 = t * BC;
@@ -356,11 +389,20 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
     }
     if constexpr (BC == 64) {
       if (tail32) {
-        const int t = ntiles - 1;
         __syncthreads();
+        if (t + 1 < ntiles) fetch(t + 1);
         const uint16_t* sk = smem + (t & 1) * SM::STAGE;
         tile_step_fwd<D, DT, CAUSAL, QB, 32, SM::KSTR, SM::VSTR>(t == 0, true, sk, sk + SM::KTILE, t * BC,
                                                                  Nb, qw0, lane, a.c, qf, oacc, m_run, l_run);
+        if (t + 1 < ntiles) stash((t + 1) & 1);
+        ++t;
+      }
+    }
+    for (; t < ntiles; ++t) {
+      __syncthreads();
+      if (t + 1 < ntiles) {
+        fetch(t + 1);
+        stash((t + 1) & 1);
       }
     }
   } else {

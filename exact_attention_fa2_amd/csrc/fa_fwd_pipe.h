@@ -25,21 +25,6 @@ namespace fa {
 
 constexpr float kRescaleGap = 8.0f;  // raise the running max only when it grows by more than this (log2)
 
-// XOR swizzle of the 16-byte chunk slot of row r. LDS has 64 banks; a 16-byte
-// read is served 16 lanes at a time and an 8-byte transposing read 32 lanes
-// at a time, so the slot must (a) differ over 16 consecutive rows read at
-// the same chunk (K operand) and (b) spread 4 aligned rows x 4 aligned
-// chunks over 16 distinct bank groups (V operand). With 256-byte rows (d=128)
-// the bank group is the slot itself; with 128-byte rows (d=64) it is the
-// slot plus 8 for odd rows.
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128)
-    return 4 * (r & 3) + ((r >> 2) & 3);
-  else
-    return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
-}
-
 template <int D, int BC>
 struct PipeSmem {
   static constexpr int TILE = BC * D;  // halves per K or V tile (unpadded)

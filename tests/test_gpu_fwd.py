@@ -181,6 +181,60 @@ def test_side_stream():
 
 
 # ---------------------------------------------------------------------------
+# properties that hold at any size, checked on the GPU result
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,causal,sqk", [("f16", False, 1.0), ("bf16", True, 3.0)])
+def test_gpu_lse_normalises_rows(dtype, causal, sqk):
+    # with the GPU's LSE, sum_j exp(s_ij - LSE_i) over the visible keys is 1
+    # (s in fp64 from the same input bits); 1e-3 in LSE allows 1.1e-3 here
+    say(f"[property] rows sum to 1 with the GPU LSE, {dtype} causal={causal}")
+    B, H, N, d = 1, 4, 700, 64
+    q, k, v = inputs.make_qkv(B, H, N, d, dtype, 71, sigma_qk=sqk)
+    sc = d ** -0.5
+    _, lse = _gpu(q, k, v, causal, sc)
+    qd, kd = P.decode(q, dtype), P.decode(k, dtype)
+    s = np.einsum("bhid,bhjd->bhij", qd, kd) * sc
+    if causal:
+        s = np.where(np.tril(np.ones((N, N), dtype=bool)), s, -np.inf)
+    tot = np.exp(s - P.to64(lse)[..., None]).sum(-1)
+    assert np.abs(tot - 1.0).max() <= 1.1e-3, np.abs(tot - 1.0).max()
+
+
+def _grid(shape, seed, lo=-4.0, hi=4.0, step=1 / 64):
+    # values on a coarse grid: sums and shifts of them stay exact in fp16
+    g = torch.Generator().manual_seed(seed)
+    n = int(round((hi - lo) / step))
+    return (torch.randint(0, n + 1, shape, generator=g).double() * step + lo).half()
+
+
+def test_gpu_invariants():
+    say("[property] key/value permutation, key shift, linearity in V")
+    B, H, N, d, sc = 1, 2, 333, 64, 0.125
+    q, k, v = (_grid((B, H, N, d), s) for s in (81, 82, 83))
+    o, lse = _gpu(q, k, v, False, sc)
+    # permuting K and V rows jointly leaves O and LSE unchanged
+    perm = torch.randperm(N, generator=torch.Generator().manual_seed(84))
+    o_p, lse_p = _gpu(q, k[:, :, perm].contiguous(), v[:, :, perm].contiguous(), False, sc)
+    P.gate_o(P.to64(o_p), P.to64(o), "f16")
+    P.gate_lse(P.to64(lse_p), P.to64(lse))
+    # K_j -> K_j + c for every j: O unchanged, LSE_i shifted by scale <q_i, c>
+    cvec = _grid((d,), 85, -1.0, 1.0, 1 / 8)
+    o_s, lse_s = _gpu(q, (k.double() + cvec.double()).half(), v, False, sc)
+    assert torch.equal((k.double() + cvec.double()).half().double(), k.double() + cvec.double())
+    P.gate_o(P.to64(o_s), P.to64(o), "f16")
+    shift = (q.double() @ cvec.double()).numpy() * sc
+    P.gate_lse(P.to64(lse_s), P.to64(lse) + shift)
+    # O is linear in V: O(V1 + V2) = O(V1) + O(V2) (V1 + V2 exact in fp16)
+    v2 = _grid((B, H, N, d), 86)
+    o_2, _ = _gpu(q, k, v2, False, sc)
+    o_12, _ = _gpu(q, k, (v.double() + v2.double()).half(), False, sc)
+    ref = P.to64(o) + P.to64(o_2)
+    err = np.abs(P.to64(o_12) - ref)
+    bound = 3 * P.ATOL["f16"] + 1.5 * P.ulp(ref, "f16")
+    assert (err <= bound).all(), float(err.max())
+
+
+# ---------------------------------------------------------------------------
 # layouts at the boundary: [B, N, H, d] and packed QKV [B, N, 3, H, d]
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("causal", [False, True])
