@@ -455,214 +455,3 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
 }
 
 }  // namespace fa
-
-namespace fa {
-
-// The same forward with the keys of every query block split between two
-// waves ("key halves"), for grids with too few query blocks to give each
-// SIMD more than one or two waves (short sequences, e.g. N = 400). Wave w
-// owns query rows (w mod NQ) and, of the key tiles, those with index
-// t = 2i + (w / NQ): the two halves walk alternate 64-key tiles of the same
-// K/V stream, which is staged two tiles per barrier. Each half keeps its own
-// running max, sums and output accumulator (a partial online softmax over
-// its keys, "FlashAttention explainer" section 4.3); at the end the second
-// half hands (m, l, acc) to the first through LDS and the first merges them
-// with the same rescale, acc = acc0 * 2^(m0 - m) + acc1 * 2^(m1 - m), before
-// the usual epilogue. Twice the waves per query block halves each wave's
-// chain of dependent tiles.
-template <int D, int DT, bool CAUSAL, int NQ>
-__global__ __launch_bounds__(2 * NQ * 64) void fa_fwd_split_kernel(const FwdArgs a) {
-  constexpr int NW = 2 * NQ, NT = NW * 64, QW = 32, BC = 64;
-  constexpr int DB = D / 32, KK = D / 16;
-  constexpr int TCH = BC * D / 8;          // 16-byte chunks per tensor per tile
-  constexpr int CH = 2 * TCH / NT;         // chunks per thread per tensor per stage (two tiles)
-  static_assert(2 * TCH % NT == 0, "stage must split evenly over threads");
-  using SM = FwdSmem<D, BC>;
-  constexpr int STAGE2 = 2 * SM::STAGE;    // halves per stage: tiles 2i and 2i+1
-  constexpr int MERGE_FLOATS = (16 * DB + 3) * 64;  // one wave's hand-over, lane-major
-  static_assert(NQ * MERGE_FLOATS * 4 <= 2 * STAGE2 * 2, "hand-over must fit in the staging area");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE2];
-
-  // ---- workgroup -> (batch, head, query block), XCD-aware ----
-  const int per = gridDim.x >> 3;
-  const int bid = blockIdx.x;
-  const int lid = (bid & 7) * per + (bid >> 3);
-  if (lid >= a.total) return;
-  const int bh = lid / a.nqb;
-  const int qi = lid - bh * a.nqb;
-  const int qblk = CAUSAL ? (a.nqb - 1 - qi) : qi;
-  const int b = bh / a.H, h = bh - b * a.H;
-
-  int64_t row0 = 0;
-  int Nb = a.N;
-  if (a.cu_seqlens) {
-    row0 = a.cu_seqlens[b];
-    Nb = a.cu_seqlens[b + 1] - (int)row0;
-  }
-  const int br = a.br;
-  if (qblk * br >= Nb) return;  // uniform over the workgroup
-
-  const uint16_t* Qg = a.q + b * a.q_sb + h * a.q_sh + row0 * a.q_sr;
-  const uint16_t* Kg = a.k + b * a.k_sb + h * a.k_sh + row0 * a.k_sr;
-  const uint16_t* Vg = a.v + b * a.v_sb + h * a.v_sh + row0 * a.v_sr;
-  uint16_t* Og = a.o + b * a.o_sb + h * a.o_sh + row0 * a.o_sr;
-  float* Lg = a.lse + b * a.lse_sb + h * a.lse_sh + row0;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
-  const int wq = w % NQ, half = w / NQ;  // wave-uniform
-  const int l32 = lane & 31, hh = lane >> 5;
-  const int qw0 = qblk * br + wq * QW;
-  const bool live = wq * QW < br && qw0 < Nb;
-
-  u32x4 qf[1][KK];
-  {
-    const int r = qw0 + l32;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const u32x4 x = *(const u32x4*)(Qg + min(r, Nb - 1) * a.q_sr + 16 * kk + 8 * hh);
-      qf[0][kk] = (r < Nb ? x : u32x4{0u, 0u, 0u, 0u}) ^ a.qsign;
-    }
-  }
-
-  const int kv_end = CAUSAL ? min(Nb, (qblk + 1) * br) : Nb;
-  const int ntiles = (kv_end + BC - 1) / BC;
-  const int nstages = (ntiles + 1) / 2;
-
-  // ---- staging of tiles 2i, 2i+1: chunk ci of the stage lies in tile ci / TCH ----
-  uint32_t koff[CH], voff[CH];
-  int soff_k[CH], soff_v[CH], stile[CH];
-#pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int ci = tid + NT * c;
-    const int tt = ci / TCH, rc = ci % TCH;
-    const int r = rc / (D / 8), col = (rc % (D / 8)) * 8;
-    stile[c] = tt;
-    koff[c] = (uint32_t)(r * (a.k_sr * 2) + col * 2);
-    voff[c] = (uint32_t)(r * (a.v_sr * 2) + col * 2);
-    soff_k[c] = tt * SM::STAGE + r * SM::KSTR + col;
-    soff_v[c] = tt * SM::STAGE + SM::KTILE + r * SM::VSTR + col;
-  }
-  u32x4 kst[CH], vst[CH];
-  auto fetch = [&](int i) __attribute__((always_inline)) {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int t = 2 * i + stile[c];  // uniform over each wave
-      const int rows = max(0, min(kv_end - t * BC, BC));
-      const int nk = rows > 0 ? (int)((rows - 1) * (a.k_sr * 2) + D * 2) : 0;
-      const int nv = rows > 0 ? (int)((rows - 1) * (a.v_sr * 2) + D * 2) : 0;
-      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(Kg + (int64_t)t * BC * a.k_sr), (short)0, nk, kBufferDword3);
-      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(Vg + (int64_t)t * BC * a.v_sr), (short)0, nv, kBufferDword3);
-      kst[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff[c], 0, 0));
-      vst[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff[c], 0, 0));
-    }
-  };
-  auto stash = [&](int buf) __attribute__((always_inline)) {
-    uint16_t* st = smem + buf * STAGE2;
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      *(u32x4*)(st + soff_k[c]) = kst[c];
-      *(u32x4*)(st + soff_v[c]) = vst[c];
-    }
-  };
-
-  f32x16 oacc[1][DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[0][db][r] = 0.f;
-  float m_run[1] = {-INFINITY}, l_run[2][1] = {{0.f}, {0.f}};
-
-  fetch(0);
-  stash(0);
-
-  // this wave's tiles: t = 2i + half below its own end (causal: its diagonal)
-  int i = 0;
-  if (live) {
-    const int wave_end = CAUSAL ? min(kv_end, qw0 + QW) : kv_end;
-    const int wnt = (wave_end + BC - 1) / BC;
-    const bool tail32 = wave_end - (wnt - 1) * BC <= 32;
-    const int nfull = tail32 ? wnt - 1 : wnt;  // tiles computed at full width
-    const int ifull = nfull > half ? (nfull - half + 1) / 2 : 0;
-    const bool has_tail = tail32 && ((wnt - 1) & 1) == half;
-    for (; i < ifull; ++i) {
-      __syncthreads();
-      if (i + 1 < nstages) fetch(i + 1);
-      const int t = 2 * i + half, key0 = t * BC;
-      const uint16_t* sk = smem + (i & 1) * STAGE2 + half * SM::STAGE;
-      const bool need_mask = (key0 + BC > Nb) || (CAUSAL && key0 + BC - 1 > qw0);
-      tile_step_fwd<D, DT, CAUSAL, 1, BC, SM::KSTR, SM::VSTR>(i == 0, need_mask, sk, sk + SM::KTILE, key0, Nb,
-                                                              qw0, lane, a.c, qf, oacc, m_run, l_run);
-      if (i + 1 < nstages) stash((i + 1) & 1);
-    }
-    if (has_tail) {
-      __syncthreads();
-      if (i + 1 < nstages) fetch(i + 1);
-      const int t = 2 * i + half;
-      const uint16_t* sk = smem + (i & 1) * STAGE2 + half * SM::STAGE;
-      tile_step_fwd<D, DT, CAUSAL, 1, 32, SM::KSTR, SM::VSTR>(i == 0, true, sk, sk + SM::KTILE, t * BC, Nb, qw0,
-                                                              lane, a.c, qf, oacc, m_run, l_run);
-      if (i + 1 < nstages) stash((i + 1) & 1);
-      ++i;
-    }
-  }
-  for (; i < nstages; ++i) {
-    __syncthreads();
-    if (i + 1 < nstages) {
-      fetch(i + 1);
-      stash((i + 1) & 1);
-    }
-  }
-
-  // ---- hand-over: the second key half to the first, through LDS ----
-  __syncthreads();  // every wave is done with the staged tiles
-  float* mg = reinterpret_cast<float*>(smem) + wq * MERGE_FLOATS;
-  if (live && half == 1) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mg[(db * 16 + r) * 64 + lane] = oacc[0][db][r];
-    mg[(16 * DB) * 64 + lane] = m_run[0];
-    mg[(16 * DB + 1) * 64 + lane] = l_run[0][0];
-    mg[(16 * DB + 2) * 64 + lane] = l_run[1][0];
-  }
-  __syncthreads();
-  if (!live || half == 1) return;
-  {
-    const float m1 = mg[(16 * DB) * 64 + lane];
-    const float m = fmaxf(m_run[0], m1);
-    // a half that saw no key has m = -inf and zero sums: its factor is 0
-    const float a0 = m_run[0] == -INFINITY ? 0.f : fast_exp2(m_run[0] - m);
-    const float a1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - m);
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[0][db][r] = oacc[0][db][r] * a0 + mg[(db * 16 + r) * 64 + lane] * a1;
-    l_run[0][0] = l_run[0][0] * a0 + mg[(16 * DB + 1) * 64 + lane] * a1;
-    l_run[1][0] = l_run[1][0] * a0 + mg[(16 * DB + 2) * 64 + lane] * a1;
-    m_run[0] = m;
-  }
-
-  // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----
-  const float l_tot = l_run[0][0] + xor_lane32(l_run[0][0]);
-  const float l_lse = DT == DT_F16 ? l_tot : l_run[1][0] + xor_lane32(l_run[1][0]);
-  const float inv = 1.f / l_tot;
-  const int qrow = qw0 + l32;
-  if (qrow < Nb) {
-    uint16_t* orow = Og + qrow * a.o_sr;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        u32x2 x;
-        x[0] = pack2<DT>(oacc[0][db][4 * g4 + 0] * inv, oacc[0][db][4 * g4 + 1] * inv);
-        x[1] = pack2<DT>(oacc[0][db][4 * g4 + 2] * inv, oacc[0][db][4 * g4 + 3] * inv);
-        *(u32x2*)(orow + db * 32 + 8 * g4 + 4 * hh) = x;
-      }
-    if (hh == 0) Lg[qrow] = (m_run[0] + fast_log2(l_lse)) * kLn2;
-  }
-}
-
-}  // namespace fa
