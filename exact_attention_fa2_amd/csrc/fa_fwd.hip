@@ -3,7 +3,6 @@
 
 #include "fa.h"
 #include "fa_fwd_kernel.h"
-#include "fa_fwd_pipe.h"
 #include "fa_launch.h"
 
 namespace fa {
@@ -32,43 +31,17 @@ int launch_one(FwdArgs a, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
-template <int D, int DT, bool CAUSAL, int NW, int QB, int BC>
-int launch_pipe(FwdArgs a, hipStream_t st) {
-  constexpr int BR = NW * 32 * QB;
-  a.br = BR;
-  a.nqb = (a.N + BR - 1) / BR;
-  const int64_t total = (int64_t)a.B * a.H * a.nqb;
-  if (total > (INT64_C(1) << 30)) return FA_ERR_DIM;
-  a.total = (int)total;
-  const int grid = (a.total + 7) / 8 * 8;
-  (void)hipGetLastError();
-  hipLaunchKernelGGL((fa_fwd_pipe_kernel<D, DT, CAUSAL, NW, QB, BC>), dim3(grid), dim3(NW * 64), 0, st,
-                     a);
-  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
-}
-
-// The pipelined kernel addresses K/V rows with 32-bit buffer offsets: every
-// row it may touch, up to one tile past N, must sit below 2^31 bytes.
-bool pipe_offsets_fit(const FwdArgs& a, int bc) {
-  const int64_t lim = INT64_C(1) << 31;
-  return ((int64_t)a.N + bc) * a.k_sr * 2 < lim && ((int64_t)a.N + bc) * a.v_sr * 2 < lim;
-}
-
 // Variant choice, from same-run measurements on MI355X (kernel time per
-// launch): the register-staged kernel with 8 waves (256 query rows) per
-// workgroup is fastest whenever the grid fills the chip (N=6400 d64: 219 us,
-// N=4096 d64: 310 us, N=400 x128 heads: 16.5 us, N=8192 causal d128: 640 us);
-// when B*H*ceil(N/256) is below the 256 CUs, the pipelined LDS-DMA kernel
-// with 4 waves (128 rows) halves the rows per workgroup for more parallelism
-// (N=400 x4 heads: 10.0 us vs 13.0 us); at d=128 (where the pipelined kernel
-// spills) the register-staged one with 4 waves. d=256 uses 32-key tiles.
+// launch): 8 waves (256 query rows) per workgroup whenever the grid fills the
+// chip (N=6400 d64: 206 us, N=4096 d64: 293 us, N=400 x128 heads: 15.5 us,
+// N=8192 causal d128: 632 us); when B*H*ceil(N/256) is below the 256 CUs,
+// 4 waves (128 rows) per workgroup for more parallelism (N=400 x4 heads:
+// 9.8 us vs 11.8 us). d=96 uses 4 waves (its registers allow no more); d=256
+// uses 4 waves and 32-key tiles.
 template <int D, int DT, bool CAUSAL>
 int pick(FwdArgs a, hipStream_t st) {
   const int64_t wg256 = (int64_t)a.B * a.H * ((a.N + 255) / 256);
-  if constexpr (D == 64) {
-    if (wg256 < 256 && pipe_offsets_fit(a, 64)) return launch_pipe<D, DT, CAUSAL, 4, 1, 64>(a, st);
-  }
-  if constexpr (D == 128) {
+  if constexpr (D == 64 || D == 128) {
     if (wg256 < 256) return launch_one<D, DT, CAUSAL, 4, 1, 64>(a, st);
   }
   if constexpr (D == 256)

@@ -71,21 +71,6 @@ constexpr float kPartialCap = 32768.0f;
 // addressing; loads past num_records return zero)
 constexpr int kBufferDword3 = 0x00020000;
 
-// XOR swizzle of the 16-byte chunk slot of row r. LDS has 64 banks; a 16-byte
-// read is served 16 lanes at a time and an 8-byte transposing read 32 lanes
-// at a time, so the slot must (a) differ over 16 consecutive rows read at
-// the same chunk (K operand) and (b) spread 4 aligned rows x 4 aligned
-// chunks over 16 distinct bank groups (V operand). With 256-byte rows (d=128)
-// the bank group is the slot itself; with 128-byte rows (d=64) it is the
-// slot plus 8 for odd rows.
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128)
-    return 4 * (r & 3) + ((r >> 2) & 3);
-  else
-    return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
-}
-
 template <int D, int BC>
 struct FwdSmem {
   static constexpr int KSTR = D + 8;   // padded K row (halves): conflict-free 16-byte reads
@@ -96,15 +81,10 @@ struct FwdSmem {
   static constexpr int BYTES = 2 * STAGE * 2;
 };
 
-// Offsets (halves) into an LDS K or V tile: rows padded to STR halves, or,
-// with STR == 0, unpadded rows of D halves whose 16-byte chunks are XOR
-// swizzled by swz<D> (the layout the LDS-DMA loads write).
+// Offset (halves) of (row, col) in an LDS K or V tile with rows padded to STR halves.
 template <int D, int STR>
 __device__ __forceinline__ int lds_off(int row, int col) {
-  if constexpr (STR != 0)
-    return row * STR + col;
-  else
-    return row * D + ((((col >> 3) ^ swz<D>(row))) << 3) + (col & 7);
+  return row * STR + col;
 }
 
 // One K/V tile for one wave: Sᵀ = K Qᵀ, online-softmax update, Oᵀ += Vᵀ Pᵀ.
