@@ -8,20 +8,13 @@
 namespace fa {
 namespace {
 
-// Rows per workgroup: as many blocks as NW*32*QB rows need, then the rows
-// spread evenly over them in 32-row units (N = 400 on 256-row workgroups:
-// 224 + 176 rows instead of 256 + 144), so no block waits on a fuller one.
-inline int even_rows(int N, int br_max) {
-  const int nqb = (N + br_max - 1) / br_max;
-  const int units = (N + 31) / 32;
-  return 32 * ((units + nqb - 1) / nqb);
-}
-
 template <int D, int DT, bool CAUSAL, int NW, int QB, int BC>
 int launch_one(FwdArgs a, hipStream_t st) {
-  constexpr int BR = NW * 32 * QB;
-  a.br = even_rows(a.N, BR);
-  a.nqb = (a.N + a.br - 1) / a.br;
+  // 32-row units spread evenly over as few blocks of at most NW units as
+  // cover them (N = 400 on 4-wave blocks: 3, 3, 3 and 4 units, not 4, 4, 4, 1)
+  static_assert(QB == 1, "one 32-row unit per wave");
+  a.units = (a.N + 31) / 32;
+  a.nqb = (a.units + NW - 1) / NW;
   const int64_t total = (int64_t)a.B * a.H * a.nqb;
   if (total > (INT64_C(1) << 30)) return FA_ERR_DIM;
   a.total = (int)total;

@@ -55,8 +55,8 @@ struct FwdArgs {
   const int32_t* cu_seqlens; // null: every sequence has N rows
   int B, H, N;               // N: rows per sequence (an upper bound with cu_seqlens)
   int nqb;                   // query blocks per (batch, head)
-  int br;                    // query rows per workgroup (a multiple of 32 rows per wave,
-                             // at most NW*32*QB; set so that the blocks of a head are even)
+  int units;                 // 32-row units of a sequence of N rows, ceil(N / 32); block q
+                             // owns units [q*units/nqb, (q+1)*units/nqb), at most one per wave
   int total;                 // B * H * nqb
   float c;                   // max(|scale| * log2(e), 1e-30): strictly positive
   uint32_t qsign;            // 0x80008000 when scale < 0, else 0
@@ -228,6 +228,7 @@ __device__ __forceinline__ void tile_step_fwd(bool first, bool masked, const uin
 
 template <int D, int DT, bool CAUSAL, int NW, int QB, int BC>
 __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
+  static_assert(QB == 1, "one 32-row unit per wave");
   constexpr int NT = NW * 64;
   constexpr int QW = 32 * QB;          // query rows per wave
   constexpr int BR = NW * QW;          // query rows per workgroup
@@ -255,8 +256,10 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
     row0 = a.cu_seqlens[b];
     Nb = a.cu_seqlens[b + 1] - (int)row0;
   }
-  const int br = a.br;          // rows of this workgroup (<= BR)
-  if (qblk * br >= Nb) return;  // uniform over the workgroup
+  // this block's rows: units spread evenly over the blocks of a head
+  const int u0 = (int)((int64_t)qblk * a.units / a.nqb);
+  const int u1 = (int)((int64_t)(qblk + 1) * a.units / a.nqb);
+  if (32 * u0 >= Nb) return;  // uniform over the workgroup
 
   const uint16_t* Qg = a.q + b * a.q_sb + h * a.q_sh + row0 * a.q_sr;
   const uint16_t* Kg = a.k + b * a.k_sb + h * a.k_sh + row0 * a.k_sr;
@@ -267,8 +270,8 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int qw0 = qblk * br + w * QW;  // first query row of this wave
-  const bool wave_rows = w * QW < br;   // waves beyond br only help with the loads
+  const int qw0 = 32 * u0 + w * QW;         // first query row of this wave
+  const bool wave_rows = w < u1 - u0;       // waves past the block only help with the loads
 
   // ---- Q fragments (B operand of Sᵀ = K Qᵀ), kept in registers; rows past
   // the end load row Nb-1 (in bounds) and are zeroed once the first K/V
@@ -281,7 +284,7 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
     for (int kk = 0; kk < KK; ++kk) qf[j][kk] = *(const u32x4*)(Qg + min(r, Nb - 1) * a.q_sr + 16 * kk + 8 * hh);
   }
 
-  const int kv_end = CAUSAL ? min(Nb, (qblk + 1) * br) : Nb;
+  const int kv_end = CAUSAL ? min(Nb, 32 * u1) : Nb;
   const int ntiles = (kv_end + BC - 1) / BC;
 
   // ---- global -> register staging of one K/V tile ----
