@@ -14,16 +14,26 @@ int64_t bwd_bytes(int B, int H, int N) {
   return ((int64_t)B * H * N * 4 + 255) / 256 * 256;  // D_i in fp32
 }
 
+// d = 96 and 128: dV and dK in two passes (d = 128 also 8-wave dQ blocks),
+// so that every kernel runs two waves per SIMD; at d = 64 both accumulators
+// fit one pass.
 template <int D, int DT, bool CAUSAL>
 int launch(const BwdArgs& a, hipStream_t st) {
+  constexpr int QNW = D == 128 ? 8 : 4;
   const int64_t rows = (int64_t)a.B * a.H * a.N;
   const int64_t gdot = (rows + 255) / 256;
   const int64_t gk = (int64_t)a.B * a.H * ((a.N + 127) / 128);
+  const int64_t gq = (int64_t)a.B * a.H * ((a.N + 32 * QNW - 1) / (32 * QNW));
   if (gdot > (INT64_C(1) << 31) - 1 || gk > (INT64_C(1) << 31) - 1) return FA_ERR_DIM;
   (void)hipGetLastError();
   hipLaunchKernelGGL((fa_bwd_dot_kernel<D, DT>), dim3((unsigned)gdot), dim3(256), 0, st, a);
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, DT, CAUSAL>), dim3((unsigned)gk), dim3(256), 0, st, a);
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, DT, CAUSAL>), dim3((unsigned)gk), dim3(256), 0, st, a);
+  if constexpr (D >= 96) {
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, DT, CAUSAL, BWD_DV>), dim3((unsigned)gk), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, DT, CAUSAL, BWD_DK>), dim3((unsigned)gk), dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, DT, CAUSAL, BWD_DKDV>), dim3((unsigned)gk), dim3(256), 0, st, a);
+  }
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, DT, CAUSAL, QNW>), dim3((unsigned)gq), dim3(QNW * 64), 0, st, a);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

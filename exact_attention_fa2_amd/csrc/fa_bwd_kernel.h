@@ -81,8 +81,14 @@ __device__ __forceinline__ void load_rowvals(const float* base, int hh, float (&
 }
 
 // ---- dK, dV: one workgroup per 128 keys ----
-template <int D, int DT, bool CAUSAL>
-__global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(const BwdArgs a) {
+// PART 0 computes both; PART 1 only dV (no V fragments, no dP) and PART 2
+// only dK. At d = 128 the two halves run as separate passes: each then fits
+// two waves per SIMD, where both together hold one (the K and V fragments
+// and both accumulators alone take 192 registers per lane).
+enum { BWD_DKDV = 0, BWD_DV = 1, BWD_DK = 2 };
+template <int D, int DT, bool CAUSAL, int PART>
+__global__ __launch_bounds__(256, PART == BWD_DKDV ? 1 : 2) void fa_bwd_dkdv_kernel(const BwdArgs a) {
+  constexpr bool WANT_DV = PART != BWD_DK, WANT_DK = PART != BWD_DV;
   constexpr int NW = 4, NT = 256, KK = D / 16, DB = D / 32;
   using SM = BwdSmem<D>;
   constexpr int BQ = SM::BQ, STR = SM::STR;
@@ -115,14 +121,17 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(const BwdArgs a) {
     const u32x4 xk = *(const u32x4*)(Kg + (int64_t)rr * D + 16 * kk + 8 * hh);
     const u32x4 xv = *(const u32x4*)(Vg + (int64_t)rr * D + 16 * kk + 8 * hh);
     kf[kk] = krow < N ? xk : u32x4{0u, 0u, 0u, 0u};
-    vf[kk] = krow < N ? xv : u32x4{0u, 0u, 0u, 0u};
+    if constexpr (WANT_DK) vf[kk] = krow < N ? xv : u32x4{0u, 0u, 0u, 0u};
   }
 
-  f32x16 dk[DB], dv[DB];
+  f32x16 dk[WANT_DK ? DB : 1], dv[WANT_DV ? DB : 1];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { dk[db][r] = 0.f; dv[db][r] = 0.f; }
+    for (int r = 0; r < 16; ++r) {
+      if constexpr (WANT_DK) dk[db][r] = 0.f;
+      if constexpr (WANT_DV) dv[db][r] = 0.f;
+    }
 
   // query tiles: causal blocks start at the tile holding the first key
   const int t0 = CAUSAL ? (kblk * 128) / BQ : 0;
@@ -187,13 +196,15 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(const BwdArgs a) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         const u32x4 qa = *(const u32x4*)(sq + (32 * qb + l32) * STR + 16 * kk + 8 * hh);
-        const u32x4 ga = *(const u32x4*)(sg + (32 * qb + l32) * STR + 16 * kk + 8 * hh);
         s = mfma32x32x16<DT>(qa, kf[kk], s);
-        dp = mfma32x32x16<DT>(ga, vf[kk], dp);
+        if constexpr (WANT_DK) {
+          const u32x4 ga = *(const u32x4*)(sg + (32 * qb + l32) * STR + 16 * kk + 8 * hh);
+          dp = mfma32x32x16<DT>(ga, vf[kk], dp);
+        }
       }
       float lq[16], dq[16];
       load_rowvals(sl + 32 * qb, hh, lq);
-      load_rowvals(sl + BQ + 32 * qb, hh, dq);
+      if constexpr (WANT_DK) load_rowvals(sl + BQ + 32 * qb, hh, dq);
       const bool diag = CAUSAL && qr0 < kw0 + 31;
       u32x4 pp[2], sp[2];
 #pragma unroll
@@ -210,10 +221,10 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(const BwdArgs a) {
               if (krow > qrow) p = 0.f;
             }
             pv[u] = p;
-            sv[u] = p * (dp[r] - dq[r]);
+            if constexpr (WANT_DK) sv[u] = p * (dp[r] - dq[r]);
           }
-          pp[c2][e] = pack2<DT>(pv[0], pv[1]);
-          sp[c2][e] = pack2<DT>(sv[0], sv[1]);
+          if constexpr (WANT_DV) pp[c2][e] = pack2<DT>(pv[0], pv[1]);
+          if constexpr (WANT_DK) sp[c2][e] = pack2<DT>(sv[0], sv[1]);
         }
       }
       // dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS ; k-slot 8*hh + 4*rd + e of chunk c2 is
@@ -224,12 +235,16 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(const BwdArgs a) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const int col = db * 32 + (g16 & 1) * 16 + 4 * (s16 & 3);
-          const u32x2 glo = lds_read_tr4(sg + ra * STR + col);
-          const u32x2 ghi = lds_read_tr4(sg + (ra + 8) * STR + col);
-          const u32x2 qlo = lds_read_tr4(sq + ra * STR + col);
-          const u32x2 qhi = lds_read_tr4(sq + (ra + 8) * STR + col);
-          dv[db] = mfma32x32x16<DT>(u32x4{glo[0], glo[1], ghi[0], ghi[1]}, pp[c2], dv[db]);
-          dk[db] = mfma32x32x16<DT>(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, sp[c2], dk[db]);
+          if constexpr (WANT_DV) {
+            const u32x2 glo = lds_read_tr4(sg + ra * STR + col);
+            const u32x2 ghi = lds_read_tr4(sg + (ra + 8) * STR + col);
+            dv[db] = mfma32x32x16<DT>(u32x4{glo[0], glo[1], ghi[0], ghi[1]}, pp[c2], dv[db]);
+          }
+          if constexpr (WANT_DK) {
+            const u32x2 qlo = lds_read_tr4(sq + ra * STR + col);
+            const u32x2 qhi = lds_read_tr4(sq + (ra + 8) * STR + col);
+            dk[db] = mfma32x32x16<DT>(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, sp[c2], dk[db]);
+          }
         }
       }
     }
@@ -247,26 +262,34 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(const BwdArgs a) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int col = db * 32 + 8 * g4 + 4 * hh;
-        u32x2 x, y;
-        x[0] = pack2<DT>(dk[db][4 * g4 + 0] * sk, dk[db][4 * g4 + 1] * sk);
-        x[1] = pack2<DT>(dk[db][4 * g4 + 2] * sk, dk[db][4 * g4 + 3] * sk);
-        y[0] = pack2<DT>(dv[db][4 * g4 + 0], dv[db][4 * g4 + 1]);
-        y[1] = pack2<DT>(dv[db][4 * g4 + 2], dv[db][4 * g4 + 3]);
-        *(u32x2*)(dkr + col) = x;
-        *(u32x2*)(dvr + col) = y;
+        if constexpr (WANT_DK) {
+          u32x2 x;
+          x[0] = pack2<DT>(dk[db][4 * g4 + 0] * sk, dk[db][4 * g4 + 1] * sk);
+          x[1] = pack2<DT>(dk[db][4 * g4 + 2] * sk, dk[db][4 * g4 + 3] * sk);
+          *(u32x2*)(dkr + col) = x;
+        }
+        if constexpr (WANT_DV) {
+          u32x2 y;
+          y[0] = pack2<DT>(dv[db][4 * g4 + 0], dv[db][4 * g4 + 1]);
+          y[1] = pack2<DT>(dv[db][4 * g4 + 2], dv[db][4 * g4 + 3]);
+          *(u32x2*)(dvr + col) = y;
+        }
       }
   }
 }
 
 // ---- dQ: one workgroup per 128 queries (query in the lane) ----
-template <int D, int DT, bool CAUSAL>
-__global__ __launch_bounds__(256) void fa_bwd_dq_kernel(const BwdArgs a) {
-  constexpr int NW = 4, NT = 256, BC = 64, KK = D / 16, DB = D / 32, KB = BC / 32;
+// NW waves of 32 query rows per workgroup (8 at d = 128: fewer staging
+// registers per thread keep it at two waves per SIMD).
+template <int D, int DT, bool CAUSAL, int NW>
+__global__ __launch_bounds__(NW * 64) void fa_bwd_dq_kernel(const BwdArgs a) {
+  constexpr int NT = NW * 64, BR = NW * 32, BC = 64, KK = D / 16, DB = D / 32, KB = BC / 32;
   constexpr int CH = BC * D / 8 / NT;
+  static_assert(BC * D / 8 % NT == 0, "tile must split evenly");
   using SM = FwdSmem<D, BC>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SM::STAGE];
 
-  const int nqb = (a.N + 127) / 128;
+  const int nqb = (a.N + BR - 1) / BR;
   const int bh = blockIdx.x / nqb, qblk0 = blockIdx.x - bh * nqb;
   if (bh >= a.B * a.H) return;
   const int qblk = CAUSAL ? nqb - 1 - qblk0 : qblk0;  // longest first
@@ -279,7 +302,7 @@ __global__ __launch_bounds__(256) void fa_bwd_dq_kernel(const BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int qw0 = qblk * 128 + w * 32;
+  const int qw0 = qblk * BR + w * 32;
   const int qrow = qw0 + l32;
 
   u32x4 qf[KK], gf[KK];
@@ -300,8 +323,13 @@ __global__ __launch_bounds__(256) void fa_bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqacc[db][r] = 0.f;
 
-  const int kv_end = CAUSAL ? min(N, (qblk + 1) * 128) : N;
+  const int kv_end = CAUSAL ? min(N, (qblk + 1) * BR) : N;
   const int ntiles = (kv_end + BC - 1) / BC;
+  // tiles this wave computes: causal waves stop at their own diagonal (the
+  // rest are fully masked) and then only help with the loads; waves with no
+  // rows only help with the loads
+  const int wave_end = qw0 >= N ? 0 : (CAUSAL ? min(kv_end, qw0 + 32) : kv_end);
+  const int wnt = (wave_end + BC - 1) / BC;
   u32x4 kst[CH], vst[CH];
   auto fetch = [&](int t) __attribute__((always_inline)) {
 #pragma unroll
@@ -331,7 +359,8 @@ __global__ __launch_bounds__(256) void fa_bwd_dq_kernel(const BwdArgs a) {
   fetch(0);
   stash(0);
   const int g16 = lane >> 4, s16 = lane & 15;
-  for (int t = 0; t < ntiles; ++t) {
+  int t = 0;
+  for (; t < wnt; ++t) {
     __syncthreads();
     if (t + 1 < ntiles) fetch(t + 1);
     const uint16_t* sk = smem + (t & 1) * SM::STAGE;
@@ -389,6 +418,13 @@ __global__ __launch_bounds__(256) void fa_bwd_dq_kernel(const BwdArgs a) {
         dqacc[db] = mfma32x32x16<DT>(u32x4{lo[0], lo[1], hi[0], hi[1]}, sf[ci], dqacc[db]);
       }
     if (t + 1 < ntiles) stash((t + 1) & 1);
+  }
+  for (; t < ntiles; ++t) {
+    __syncthreads();
+    if (t + 1 < ntiles) {
+      fetch(t + 1);
+      stash((t + 1) & 1);
+    }
   }
 
   if (qrow < N) {
