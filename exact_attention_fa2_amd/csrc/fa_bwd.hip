@@ -21,7 +21,7 @@ template <int D, int DT, bool CAUSAL>
 int launch(const BwdArgs& a, hipStream_t st) {
   constexpr int QNW = D == 128 ? 8 : 4;
   const int64_t rows = (int64_t)a.B * a.H * a.N;
-  const int64_t gdot = (rows + 255) / 256;
+  const int64_t gdot = (rows * bwd_dot_lanes<D>() + 255) / 256;
   const int64_t gk = (int64_t)a.B * a.H * ((a.N + 127) / 128);
   const int64_t gq = (int64_t)a.B * a.H * ((a.N + 32 * QNW - 1) / (32 * QNW));
   if (gdot > (INT64_C(1) << 31) - 1 || gk > (INT64_C(1) << 31) - 1) return FA_ERR_DIM;

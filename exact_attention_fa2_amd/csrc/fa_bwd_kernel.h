@@ -39,25 +39,41 @@ struct BwdArgs {
 };
 
 // ---- D_i = <dO_i, O_i> ----
+// G consecutive lanes (a power of two) share a row, each taking D/8/G
+// 16-byte chunks of O and dO, so a wave reads whole consecutive rows; the
+// partial dots are then summed across those lanes.
+template <int D>
+constexpr int bwd_dot_lanes() {
+  return (D / 8) % 16 == 0 ? 16 : (D / 8) % 8 == 0 ? 8 : 4;
+}
 template <int D, int DT>
 __global__ __launch_bounds__(256) void fa_bwd_dot_kernel(const BwdArgs a) {
+  constexpr int G = bwd_dot_lanes<D>();  // lanes per row
+  constexpr int CPL = D / 8 / G;                                         // chunks per lane
+  static_assert(CPL * G * 8 == D, "row must split evenly over its lanes");
   const int64_t rows = (int64_t)a.B * a.H * a.N;
-  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (r >= rows) return;
-  const uint16_t* op = a.o + r * D;
-  const uint16_t* gp = a.dout + r * D;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t r = t / G;
+  const int ln = (int)(t % G);
   float acc = 0.f;
+  if (r < rows) {
 #pragma unroll
-  for (int c = 0; c < D; c += 8) {
-    const u32x4 x = *(const u32x4*)(op + c);
-    const u32x4 y = *(const u32x4*)(gp + c);
+    for (int c = 0; c < CPL; ++c) {
+      const int col = 8 * (ln + G * c);
+      const u32x4 x = *(const u32x4*)(a.o + r * D + col);
+      const u32x4 y = *(const u32x4*)(a.dout + r * D + col);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc += to_f32<DT>((uint16_t)(x[e] & 0xFFFF)) * to_f32<DT>((uint16_t)(y[e] & 0xFFFF));
-      acc += to_f32<DT>((uint16_t)(x[e] >> 16)) * to_f32<DT>((uint16_t)(y[e] >> 16));
+      for (int e = 0; e < 4; ++e) {
+        acc += to_f32<DT>((uint16_t)(x[e] & 0xFFFF)) * to_f32<DT>((uint16_t)(y[e] & 0xFFFF));
+        acc += to_f32<DT>((uint16_t)(x[e] >> 16)) * to_f32<DT>((uint16_t)(y[e] >> 16));
+      }
     }
   }
-  a.dvec[r] = acc;
+  // G divides 64 and each row starts at a multiple of G lanes, so a row's
+  // lanes sit inside one wave
+#pragma unroll
+  for (int m = G / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  if (r < rows && ln == 0) a.dvec[r] = acc;
 }
 
 template <int D>
@@ -70,14 +86,17 @@ struct BwdSmem {
 };
 
 // 16 per-register row values for rows 8*(r/4) + 4*hh + r%4 of a 32-row block
-// starting at `base` of an fp32 LDS vector
-__device__ __forceinline__ void load_rowvals(const float* base, int hh, float (&v)[16]) {
+// starting at `base` of an fp32 LDS vector (the row layout of an MFMA
+// accumulator)
+__device__ __forceinline__ f32x16 load_rowvals(const float* base, int hh) {
+  f32x16 v;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const f32x4 x = *(const f32x4*)(base + 8 * g + 4 * hh);
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[4 * g + e] = x[e];
   }
+  return v;
 }
 
 // ---- dK, dV: one workgroup per 128 keys ----
@@ -138,7 +157,10 @@ __global__ __launch_bounds__(256, PART == BWD_DKDV ? 1 : 2) void fa_bwd_dkdv_ker
   const int nt = (N + BQ - 1) / BQ;
 
   u32x4 qs[CH], gs[CH];
+  // per query row: -LSE log2(e) / c and -D_i, the starting values of the S
+  // and dP accumulators
   float ls = 0.f, ds = 0.f;
+  const float inv_c = 1.f / a.c;
   auto fetch = [&](int t) __attribute__((always_inline)) {
     const int q0 = t * BQ;
 #pragma unroll
@@ -153,9 +175,9 @@ __global__ __launch_bounds__(256, PART == BWD_DKDV ? 1 : 2) void fa_bwd_dkdv_ker
     }
     if (tid < BQ) {
       const int gr = q0 + tid;
-      // rows past the end: a huge LSE makes their weights exactly zero
-      ls = gr < N ? Lg[gr] * kLog2e : INFINITY;
-      ds = gr < N ? Dg[gr] : 0.f;
+      // rows past the end start at -inf, which makes their weights exactly zero
+      ls = gr < N ? -Lg[gr] * kLog2e * inv_c : -INFINITY;
+      ds = gr < N ? -Dg[gr] : 0.f;
     }
   };
   auto stash = [&](int buf) __attribute__((always_inline)) {
@@ -191,8 +213,12 @@ __global__ __launch_bounds__(256, PART == BWD_DKDV ? 1 : 2) void fa_bwd_dkdv_ker
     for (int qb = 0; qb < BQ / 32; ++qb) {
       const int qr0 = q0 + 32 * qb;  // first query of this 32-row block
       if (CAUSAL && qr0 + 31 < kw0) continue;  // every query precedes every key
-      // S = Q Kᵀ and dP = dO Vᵀ, key in the lane, queries in the registers
-      f32x16 s = {}, dp = {};
+      // S = Q Kᵀ and dP = dO Vᵀ, key in the lane, queries in the registers.
+      // The accumulators start at the row terms, so that they end as
+      // S - LSE log2(e) / c (c times it is the log2 weight) and dP - D_i:
+      // no registers hold the 16 row values of each beside them.
+      f32x16 s = load_rowvals(sl + 32 * qb, hh), dp;
+      if constexpr (WANT_DK) dp = load_rowvals(sl + BQ + 32 * qb, hh);
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         const u32x4 qa = *(const u32x4*)(sq + (32 * qb + l32) * STR + 16 * kk + 8 * hh);
@@ -202,9 +228,6 @@ __global__ __launch_bounds__(256, PART == BWD_DKDV ? 1 : 2) void fa_bwd_dkdv_ker
           dp = mfma32x32x16<DT>(ga, vf[kk], dp);
         }
       }
-      float lq[16], dq[16];
-      load_rowvals(sl + 32 * qb, hh, lq);
-      if constexpr (WANT_DK) load_rowvals(sl + BQ + 32 * qb, hh, dq);
       const bool diag = CAUSAL && qr0 < kw0 + 31;
       u32x4 pp[2], sp[2];
 #pragma unroll
@@ -215,13 +238,13 @@ __global__ __launch_bounds__(256, PART == BWD_DKDV ? 1 : 2) void fa_bwd_dkdv_ker
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const int r = 8 * c2 + 2 * e + u;
-            float p = fast_exp2(__builtin_fmaf(s[r], a.c, -lq[r]));
+            float p = fast_exp2(s[r] * a.c);
             if (CAUSAL && diag) {
               const int qrow = qr0 + 8 * (r >> 2) + 4 * hh + (r & 3);
               if (krow > qrow) p = 0.f;
             }
             pv[u] = p;
-            if constexpr (WANT_DK) sv[u] = p * (dp[r] - dq[r]);
+            if constexpr (WANT_DK) sv[u] = p * dp[r];
           }
           if constexpr (WANT_DV) pp[c2][e] = pack2<DT>(pv[0], pv[1]);
           if constexpr (WANT_DK) sp[c2][e] = pack2<DT>(sv[0], sv[1]);
