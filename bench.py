@@ -18,7 +18,6 @@ from __future__ import annotations
 
 import argparse
 import hashlib
-import glob
 import json
 import math
 import os
@@ -40,11 +39,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# the sources the forward kernel is built from (its code and its dispatch)
+FWD_SOURCES = ("fa_device.h", "fa_fwd_kernel.h", "fa_fwd.hip")
+
+
 def kernel_source_hash() -> str:
+    """Hash of the forward kernel's sources: stored HBM counters are used only
+    while it matches."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "exact_attention_fa2_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode() + f.read())
+    for name in FWD_SOURCES:
+        with open(os.path.join(ROOT, "exact_attention_fa2_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
