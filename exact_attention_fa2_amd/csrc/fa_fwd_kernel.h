@@ -241,9 +241,16 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SM::STAGE];
 
   // ---- workgroup -> (batch, head, query block), XCD-aware ----
+  // Workgroups are dealt round-robin over the 8 XCDs. With equal-length
+  // sequences each XCD takes a contiguous run of whole heads, whose blocks
+  // then share K/V in that XCD's L2. Packed sequences of different lengths
+  // keep the plain order instead: a contiguous run would hand the long
+  // sequences to a few XCDs, while the plain order spreads every sequence's
+  // blocks over all eight (re-reads of K/V across XCDs hit the shared
+  // Infinity Cache).
   const int per = gridDim.x >> 3;
   const int bid = blockIdx.x;
-  const int lid = (bid & 7) * per + (bid >> 3);
+  const int lid = a.cu_seqlens ? bid : (bid & 7) * per + (bid >> 3);
   if (lid >= a.total) return;
   const int bh = lid / a.nqb;
   const int qi = lid - bh * a.nqb;
