@@ -8,7 +8,7 @@
 namespace fa {
 namespace {
 
-template <int D, int DT, bool CAUSAL, int NW, int QB, int BC>
+template <int D, int DT, bool CAUSAL, int NW, int QB, int BC, int PF>
 int launch_one(FwdArgs a, hipStream_t st) {
   // 32-row units spread evenly over as few blocks of at most NW units as
   // cover them (N = 400 on 4-wave blocks: 3, 3, 3 and 4 units, not 4, 4, 4, 1)
@@ -20,7 +20,7 @@ int launch_one(FwdArgs a, hipStream_t st) {
   a.total = (int)total;
   const int grid = (a.total + 7) / 8 * 8;  // a multiple of the 8 XCDs
   (void)hipGetLastError();
-  hipLaunchKernelGGL((fa_fwd_kernel<D, DT, CAUSAL, NW, QB, BC>), dim3(grid), dim3(NW * 64), 0, st, a);
+  hipLaunchKernelGGL((fa_fwd_kernel<D, DT, CAUSAL, NW, QB, BC, PF>), dim3(grid), dim3(NW * 64), 0, st, a);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -31,18 +31,29 @@ int launch_one(FwdArgs a, hipStream_t st) {
 // 4 waves (128 rows) per workgroup for more parallelism (N=400 x4 heads:
 // 9.8 us vs 11.8 us). d=96 uses 4 waves (its registers allow no more); d=256
 // uses 4 waves and 32-key tiles.
+//
+// K fragments are read two k-steps ahead of their MFMAs (PF = 2) wherever
+// that costs no occupancy: N=400 x4 heads fp16 -2 %, N=8192 causal d128
+// -1 %, N=400 x128 heads bf16 unchanged. The 8-wave fp16 d=64 kernel would
+// need 135 VGPRs instead of 127 and drop from 4 to 3 waves per SIMD (N=4096:
+// +7 %), so it keeps the compiler's schedule.
+template <int D, int DT, int NW>
+constexpr int k_prefetch() {
+  return (D == 64 && DT == DT_F16 && NW == 8) ? 0 : 2;
+}
+
 template <int D, int DT, bool CAUSAL>
 int pick(FwdArgs a, hipStream_t st) {
   const int64_t wg256 = (int64_t)a.B * a.H * ((a.N + 255) / 256);
   if constexpr (D == 64 || D == 128) {
-    if (wg256 < 256) return launch_one<D, DT, CAUSAL, 4, 1, 64>(a, st);
+    if (wg256 < 256) return launch_one<D, DT, CAUSAL, 4, 1, 64, k_prefetch<D, DT, 4>()>(a, st);
   }
   if constexpr (D == 256)
-    return launch_one<D, DT, CAUSAL, 4, 1, 32>(a, st);
+    return launch_one<D, DT, CAUSAL, 4, 1, 32, k_prefetch<D, DT, 4>()>(a, st);
   else if constexpr (D == 96)
-    return launch_one<D, DT, CAUSAL, 4, 1, 64>(a, st);
+    return launch_one<D, DT, CAUSAL, 4, 1, 64, k_prefetch<D, DT, 4>()>(a, st);
   else
-    return launch_one<D, DT, CAUSAL, 8, 1, 64>(a, st);
+    return launch_one<D, DT, CAUSAL, 8, 1, 64, k_prefetch<D, DT, 8>()>(a, st);
 }
 
 template <int D, int DT>

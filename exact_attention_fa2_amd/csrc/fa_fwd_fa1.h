@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256) void fa_fwd_fa1_kernel(const FwdArgs a, float*
         l_run[1][0] = wsw[(DB * 16 + 2) * 64 + lane];
       }
       const bool need_mask = (key0 + BC > Nb) || (CAUSAL && key0 + BC - 1 > qw0);
-      tile_step_fwd<D, DT, CAUSAL, QB, BC, SM::KSTR, SM::VSTR>(j == 0, need_mask, sk, sv, key0, Nb, qw0,
+      tile_step_fwd<D, DT, CAUSAL, QB, BC, SM::KSTR, SM::VSTR, 0>(j == 0, need_mask, sk, sv, key0, Nb, qw0,
                                                                lane, a.c, qf, oacc, m_run, l_run);
       const int last_j = CAUSAL ? min(ntk - 1, (qb * BR + BR - 1) / BC) : ntk - 1;
       if (j < last_j) {

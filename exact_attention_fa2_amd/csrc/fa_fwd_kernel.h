@@ -90,7 +90,7 @@ __device__ __forceinline__ int lds_off(int row, int col) {
 // One K/V tile for one wave: Sᵀ = K Qᵀ, online-softmax update, Oᵀ += Vᵀ Pᵀ.
 // Masked tiles (wave-uniform flag) apply the ragged-tail and causal masks;
 // `first` (wave-uniform) marks the first tile of the wave's rows.
-template <int D, int DT, bool CAUSAL, int QB, int BC, int KSTR, int VSTR>
+template <int D, int DT, bool CAUSAL, int QB, int BC, int KSTR, int VSTR, int PF>
 __device__ __forceinline__ void tile_step_fwd(bool first, bool masked, const uint16_t* __restrict__ sk,
                                                const uint16_t* __restrict__ sv, int key0, int Nb,
                                                int qw0, int lane, float c, const u32x4 (&qf)[QB][D / 16],
@@ -110,13 +110,39 @@ __device__ __forceinline__ void tile_step_fwd(bool first, bool masked, const uin
       for (int j = 0; j < QB; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][j][r] = 0.f;
+    if constexpr (PF > 0) {
+      // K fragments read PF k-steps ahead of the MFMAs that use them, with a
+      // scheduling fence per k-step so that the reads stay ahead (left to
+      // itself the compiler keeps about one step in flight and each MFMA pair
+      // waits out an LDS round trip)
+      u32x4 kfp[PF][KB];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
+      for (int i = 0; i < PF; ++i)
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const u32x4 ka = *(const u32x4*)(kt + lds_off<D, KSTR>(kb * 32 + l32, 16 * kk + 8 * hh));
+        for (int kb = 0; kb < KB; ++kb)
+          kfp[i][kb] = *(const u32x4*)(kt + lds_off<D, KSTR>(kb * 32 + l32, 16 * i + 8 * hh));
 #pragma unroll
-        for (int j = 0; j < QB; ++j) s[kb][j] = mfma32x32x16<DT>(ka, qf[j][kk], s[kb][j]);
+      for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int j = 0; j < QB; ++j) s[kb][j] = mfma32x32x16<DT>(kfp[kk % PF][kb], qf[j][kk], s[kb][j]);
+        if (kk + PF < KK) {
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+            kfp[kk % PF][kb] = *(const u32x4*)(kt + lds_off<D, KSTR>(kb * 32 + l32, 16 * (kk + PF) + 8 * hh));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const u32x4 ka = *(const u32x4*)(kt + lds_off<D, KSTR>(kb * 32 + l32, 16 * kk + 8 * hh));
+#pragma unroll
+          for (int j = 0; j < QB; ++j) s[kb][j] = mfma32x32x16<DT>(ka, qf[j][kk], s[kb][j]);
+        }
       }
     }
     if (masked) {
@@ -226,7 +252,7 @@ __device__ __forceinline__ void tile_step_fwd(bool first, bool masked, const uin
   }
 }
 
-template <int D, int DT, bool CAUSAL, int NW, int QB, int BC>
+template <int D, int DT, bool CAUSAL, int NW, int QB, int BC, int PF>
 __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
   static_assert(QB == 1, "one 32-row unit per wave");
   constexpr int NT = NW * 64;
@@ -377,7 +403,7 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
       const uint16_t* sv = sk + SM::KTILE;
       // ragged last tile, or (causal) keys after some query of this wave
       const bool need_mask = (key0 + BC > Nb) || (CAUSAL && key0 + BC - 1 > qw0);
-      tile_step_fwd<D, DT, CAUSAL, QB, BC, SM::KSTR, SM::VSTR>(t == 0, need_mask, sk, sv, key0, Nb, qw0,
+      tile_step_fwd<D, DT, CAUSAL, QB, BC, SM::KSTR, SM::VSTR, PF>(t == 0, need_mask, sk, sv, key0, Nb, qw0,
                                                                lane, a.c, qf, oacc, m_run, l_run);
       if (t + 1 < ntiles) stash((t + 1) & 1);
     }
@@ -386,7 +412,7 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
         __syncthreads();
         if (t + 1 < ntiles) fetch(t + 1);
         const uint16_t* sk = smem + (t & 1) * SM::STAGE;
-        tile_step_fwd<D, DT, CAUSAL, QB, 32, SM::KSTR, SM::VSTR>(t == 0, true, sk, sk + SM::KTILE, t * BC,
+        tile_step_fwd<D, DT, CAUSAL, QB, 32, SM::KSTR, SM::VSTR, PF>(t == 0, true, sk, sk + SM::KTILE, t * BC,
                                                                  Nb, qw0, lane, a.c, qf, oacc, m_run, l_run);
         if (t + 1 < ntiles) stash((t + 1) & 1);
         ++t;
