@@ -24,7 +24,8 @@ int launch(const BwdArgs& a, hipStream_t st) {
   const int64_t gdot = (rows * bwd_dot_lanes<D>() + 255) / 256;
   const int64_t gk = (int64_t)a.B * a.H * ((a.N + 127) / 128);
   const int64_t gq = (int64_t)a.B * a.H * ((a.N + 32 * QNW - 1) / (32 * QNW));
-  if (gdot > (INT64_C(1) << 31) - 1 || gk > (INT64_C(1) << 31) - 1) return FA_ERR_DIM;
+  if (gdot > (INT64_C(1) << 31) - 1 || gk > (INT64_C(1) << 31) - 1 || gq > (INT64_C(1) << 31) - 1)
+    return FA_ERR_DIM;
   (void)hipGetLastError();
   hipLaunchKernelGGL((fa_bwd_dot_kernel<D, DT>), dim3((unsigned)gdot), dim3(256), 0, st, a);
   if constexpr (D >= 96) {

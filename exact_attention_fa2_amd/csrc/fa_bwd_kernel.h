@@ -6,7 +6,8 @@
 //   dV = Pᵀ dO,  dS = P ∘ (dP - D),  D_i = <dO_i, O_i>,
 //   dK = scale · dSᵀ Q,  dQ = scale · dS K.
 //
-// MI355X layout (our design): three kernels and no atomics.
+// MI355X layout (our design): three kernels (the dK/dV one as two passes,
+// dV then dK, at d = 96 and 128) and no atomics.
 //  * fa_bwd_dot_kernel: D_i in fp32.
 //  * fa_bwd_dkdv_kernel: one workgroup per block of 128 keys, each wave owning
 //    32 keys whose K and V fragments stay in registers; 64-query tiles of Q,

@@ -34,8 +34,11 @@
 //    as zero with no per-lane test) while tile t is computed from the other
 //    half of a double-buffered LDS, one barrier per tile.
 //  * Workgroup ids are remapped so that each XCD (workgroups are dealt
-//    round-robin over the 8 XCDs) walks whole heads, sharing K/V in its L2;
-//    causal blocks run longest first.
+//    round-robin over the 8 XCDs) walks whole heads, sharing K/V in its L2
+//    (packed batches of unequal sequences keep the plain order); causal
+//    blocks run longest first.
+//  * A head's 32-row units are spread evenly over its blocks, one unit per
+//    wave; waves without a unit only help with the K/V loads.
 #pragma once
 #include "fa_device.h"
 
