@@ -3,6 +3,7 @@
 
 #include "fa.h"
 #include "fa_fwd_kernel.h"
+#include "fa_fwd_split.h"
 #include "fa_launch.h"
 
 namespace fa {
@@ -24,6 +25,21 @@ int launch_one(FwdArgs a, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+// Key-split kernel: one workgroup of NS waves per 32-row unit, the unit's
+// keys split over the waves.
+template <int D, int DT, bool CAUSAL, int NS>
+int launch_split(FwdArgs a, hipStream_t st) {
+  a.units = (a.N + 31) / 32;
+  a.nqb = 1;
+  const int64_t total = (int64_t)a.B * a.H * a.units;
+  if (total > (INT64_C(1) << 30)) return FA_ERR_DIM;
+  a.total = (int)total;
+  const int grid = (a.total + 7) / 8 * 8;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL((fa_fwd_split_kernel<D, DT, CAUSAL, NS, 2>), dim3(grid), dim3(NS * 64), 0, st, a);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 // Variant choice, from same-run measurements on MI355X (kernel time per
 // launch): 8 waves (256 query rows) per workgroup whenever the grid fills the
 // chip (N=6400 d64: 206 us, N=4096 d64: 293 us, N=400 x128 heads: 15.5 us,
@@ -31,6 +47,13 @@ int launch_one(FwdArgs a, hipStream_t st) {
 // 4 waves (128 rows) per workgroup for more parallelism (N=400 x4 heads:
 // 9.8 us vs 11.8 us). d=96 uses 4 waves (its registers allow no more); d=256
 // uses 4 waves and 32-key tiles.
+//
+// At d=64, when the 4-wave kernel would launch at most 128 workgroups (half
+// the CUs or fewer), the key-split kernel runs instead: N=400 x4 heads fp16
+// 8.1 vs 9.8 us, N=400 x16 heads bf16 8.7 vs 10.4 us, N=4096 x2 heads 29.8
+// vs 55.8 us. With 256 workgroups the split loses (N=8192 x4 heads: 204 vs
+// 115-128 us): it has 4x less reuse of each K/V tile, and its 128 KB of LDS
+// allow one workgroup per CU. At d=128 it did not pay in the shapes tried.
 //
 // K fragments are read two k-steps ahead of their MFMAs (PF = 2) wherever
 // that costs no occupancy: N=400 x4 heads fp16 -2 %, N=8192 causal d128
@@ -45,6 +68,9 @@ constexpr int k_prefetch() {
 template <int D, int DT, bool CAUSAL>
 int pick(FwdArgs a, hipStream_t st) {
   const int64_t wg256 = (int64_t)a.B * a.H * ((a.N + 255) / 256);
+  if constexpr (D == 64) {
+    if ((int64_t)a.B * a.H * ((a.N + 127) / 128) <= 128) return launch_split<D, DT, CAUSAL, 4>(a, st);
+  }
   if constexpr (D == 64 || D == 128) {
     if (wg256 < 256) return launch_one<D, DT, CAUSAL, 4, 1, 64, k_prefetch<D, DT, 4>()>(a, st);
   }

@@ -84,10 +84,31 @@ struct FwdSmem {
   static constexpr int BYTES = 2 * STAGE * 2;
 };
 
-// Offset (halves) of (row, col) in an LDS K or V tile with rows padded to STR halves.
+// XOR swizzle of the 16-byte chunk slot of row r in an unpadded LDS tile
+// (rows of D halves). LDS has 64 banks; a 16-byte read is served 16 lanes at
+// a time and an 8-byte transposing read 32 lanes at a time, so the slot must
+// (a) differ over 16 consecutive rows read at the same chunk (the K operand)
+// and (b) spread 4 aligned rows x 4 aligned chunks over 16 distinct bank
+// groups (the V operand). With 256-byte rows (d=128) the bank group is the
+// slot itself; with 128-byte rows (d=64) it is the slot plus 8 for odd rows.
+template <int D>
+__device__ __forceinline__ int lds_swz(int r) {
+  static_assert(D == 64 || D == 128, "swizzled tiles are laid out for d = 64 and 128");
+  if constexpr (D == 128)
+    return 4 * (r & 3) + ((r >> 2) & 3);
+  else
+    return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+
+// Offset (halves) of (row, col) in an LDS K or V tile: rows padded to STR
+// halves, or, with STR = 0, unpadded rows of D halves whose 16-byte chunks
+// are XOR-swizzled (the layout that whole-row LDS-DMA writes can produce).
 template <int D, int STR>
 __device__ __forceinline__ int lds_off(int row, int col) {
-  return row * STR + col;
+  if constexpr (STR == 0)
+    return row * D + (((col >> 3) ^ lds_swz<D>(row)) << 3) + (col & 7);
+  else
+    return row * STR + col;
 }
 
 // One K/V tile for one wave: Sᵀ = K Qᵀ, online-softmax update, Oᵀ += Vᵀ Pᵀ.

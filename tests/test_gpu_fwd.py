@@ -57,6 +57,19 @@ def test_workload_parity(name, seed):
     say(f"  {name} seed {seed}: max|dO| {eo:.3e}  max|dLSE| {el:.3e}")
 
 
+# The d=64 dispatch switches from the key-split kernel (one workgroup per
+# 32-row unit, keys split over 4 waves) to the main kernel when
+# B*H*ceil(N/128) passes 128. Both sides of the boundary, against the oracle;
+# a few long rows split over the waves with large logits (rescale in the
+# merge), and sequences whose tiles leave some waves without keys.
+@pytest.mark.parametrize("H,N,dtype,causal", [(128, 128, "f16", False), (129, 128, "bf16", True),
+                                              (2, 4096, "bf16", False), (1, 3000, "f16", True),
+                                              (3, 100, "bf16", True), (4, 192, "f16", False)])
+def test_key_split_path(H, N, dtype, causal):
+    rows = P.sample_rows(1, H, N, 300, H + N) if H * N * N > 4 * 1024 * 1024 else None
+    run_case(1, H, N, 64, dtype, causal, 40 + H, None, 2.5, 1.0, rows)
+
+
 def test_long_causal_variance3_reading():
     # the other reading of the large-logit workload: variance 3 (sigma = sqrt 3)
     w = inputs.WORKLOADS["n8192_causal"]
@@ -275,6 +288,28 @@ def test_packed_qkv_pages_shape(d):
 # ---------------------------------------------------------------------------
 # variable-length packed batches
 # ---------------------------------------------------------------------------
+def test_varlen_small_grid():
+    # few short sequences: the key-split kernel's varlen path
+    seqlens = [400, 0, 37, 129]
+    say(f"[fa_fwd_varlen] {seqlens} d=64 bf16 causal=False/True")
+    H = 2
+    q, k, v, cu = inputs.make_varlen(seqlens, H, 64, "bf16", 82)
+    qd, kd, vd = (P.decode(x, "bf16") for x in (q, k, v))
+    for causal in (False, True):
+        o, lse = fa.attention_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), max(seqlens), causal=causal)
+        torch.cuda.synchronize()
+        og, lg = P.to64(o), P.to64(lse)
+        for b, n in enumerate(seqlens):
+            if n == 0:
+                continue
+            s0 = int(cu[b])
+            sl = slice(s0, s0 + n)
+            t = lambda x: x[sl].transpose(1, 0, 2)[None]
+            ro, rl = oracle.attention_fwd(t(qd), t(kd), t(vd), 0.125, causal)
+            P.gate_o(og[sl].transpose(1, 0, 2)[None], ro, "bf16", what=f"O seq {b}")
+            P.gate_lse(lg[:, sl][None], rl)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d,dtype", [(64, "f16"), (128, "bf16")])
 def test_varlen(causal, d, dtype):
