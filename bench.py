@@ -40,7 +40,7 @@ def log(*a):
 
 
 # the sources the forward kernel is built from (its code and its dispatch)
-FWD_SOURCES = ("fa_device.h", "fa_fwd_kernel.h", "fa_fwd.hip")
+FWD_SOURCES = ("fa_device.h", "fa_fwd_kernel.h", "fa_fwd.hip", "fa_fwd_split.h")
 
 
 def kernel_source_hash() -> str:
