@@ -36,7 +36,7 @@ int launch_split(FwdArgs a, hipStream_t st) {
   a.total = (int)total;
   const int grid = (a.total + 7) / 8 * 8;
   (void)hipGetLastError();
-  hipLaunchKernelGGL((fa_fwd_split_kernel<D, DT, CAUSAL, NS, 2>), dim3(grid), dim3(NS * 64), 0, st, a);
+  hipLaunchKernelGGL((fa_fwd_split_kernel<D, DT, CAUSAL, NS, 1, 2>), dim3(grid), dim3(NS * 64), 0, st, a);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -48,12 +48,16 @@ int launch_split(FwdArgs a, hipStream_t st) {
 // 9.8 us vs 11.8 us). d=96 uses 4 waves (its registers allow no more); d=256
 // uses 4 waves and 32-key tiles.
 //
-// At d=64, when the 4-wave kernel would launch at most 128 workgroups (half
-// the CUs or fewer), the key-split kernel runs instead: N=400 x4 heads fp16
-// 8.1 vs 9.8 us, N=400 x16 heads bf16 8.7 vs 10.4 us, N=4096 x2 heads 29.8
-// vs 55.8 us. With 256 workgroups the split loses (N=8192 x4 heads: 204 vs
-// 115-128 us): it has 4x less reuse of each K/V tile, and its 128 KB of LDS
-// allow one workgroup per CU. At d=128 it did not pay in the shapes tried.
+// The key-split kernel (4 waves per 32-row unit, one K/V buffer per wave)
+// runs while its B*H*ceil(N/32) workgroups all fit the chip at once: at most
+// 512 at d=64 (64 KB of LDS each, two per CU), 256 at d=128 (128 KB, one per
+// CU). Against the 4-wave kernel, same box: d=64 N=400 x4 heads 8.1 vs
+// 9.8 us, N=4096 x2 heads 30.4 vs 56.6 us, N=512 x32 heads 11.0 vs 11.9 us;
+// d=128 N=2048 x4 heads 33.2 vs 46.4 us, N=4096 x2 heads causal 52.2 vs
+// 85.1 us, N=400 x8 heads 12.8 vs 14.2 us. Past that size it loses (d=64
+// N=512 x64 heads 19.8 vs 13.5 us; d=128 N=1024 x16 heads 38.0 vs 27.4 us):
+// each K/V tile is reused 4x less, and a second round of workgroups follows
+// the first.
 //
 // K fragments are read two k-steps ahead of their MFMAs (PF = 2) wherever
 // that costs no occupancy: N=400 x4 heads fp16 -2 %, N=8192 causal d128
@@ -68,8 +72,11 @@ constexpr int k_prefetch() {
 template <int D, int DT, bool CAUSAL>
 int pick(FwdArgs a, hipStream_t st) {
   const int64_t wg256 = (int64_t)a.B * a.H * ((a.N + 255) / 256);
-  if constexpr (D == 64) {
-    if ((int64_t)a.B * a.H * ((a.N + 127) / 128) <= 128) return launch_split<D, DT, CAUSAL, 4>(a, st);
+  if constexpr (D == 64 || D == 128) {
+    // key-split kernel while all its workgroups fit the chip at once (64 KB
+    // of LDS each at d=64: two per CU; 128 KB at d=128: one)
+    constexpr int64_t kSplitMax = D == 64 ? 512 : 256;
+    if ((int64_t)a.B * a.H * ((a.N + 31) / 32) <= kSplitMax) return launch_split<D, DT, CAUSAL, 4>(a, st);
   }
   if constexpr (D == 64 || D == 128) {
     if (wg256 < 256) return launch_one<D, DT, CAUSAL, 4, 1, 64, k_prefetch<D, DT, 4>()>(a, st);

@@ -14,8 +14,8 @@
 //  * One workgroup per (batch, head, 32-row unit); wave s takes a contiguous
 //    run of the unit's 64-key tiles.
 //  * Each wave moves its own K/V tiles HBM -> LDS with buffer_load ... lds
-//    (LDS-DMA: no staging registers, no address VALU) into its own
-//    double-buffered LDS region of unpadded, XOR-swizzled rows. No other wave
+//    (LDS-DMA: no staging registers, no address VALU) into its own LDS region
+//    (NB = 1 or 2 buffers) of unpadded, XOR-swizzled rows. No other wave
 //    reads that region, so a wave only waits for its own loads (vmcnt); the
 //    workgroup synchronises once, for the merge.
 //  * The tile step is the main kernel's (scores, online softmax, PV product).
@@ -33,11 +33,11 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-template <int D, int NS>
+template <int D, int NS, int NB>
 struct SplitSmem {
   static constexpr int BC = 64;
   static constexpr int TILE = BC * D;           // halves per unpadded K or V tile
-  static constexpr int WAVE = 4 * TILE;         // K and V, two buffers each
+  static constexpr int WAVE = 2 * NB * TILE;    // K and V, NB buffers each
   static constexpr int HALVES = NS * WAVE;
   // merge area (floats, reusing the tiles): per wave and lane DB*16
   // accumulators, m and the two sums, stored element-major
@@ -45,11 +45,11 @@ struct SplitSmem {
   static_assert(NS * PART * 64 * 2 <= HALVES, "partials must fit in the tile area");
 };
 
-template <int D, int DT, bool CAUSAL, int NS, int PF>
+template <int D, int DT, bool CAUSAL, int NS, int NB, int PF>
 __global__ __launch_bounds__(NS * 64) void fa_fwd_split_kernel(const FwdArgs a) {
   constexpr int BC = 64, KK = D / 16, DB = D / 32, CPR = D / 8;
   constexpr int LOADS = BC * CPR / 64;  // DMA loads per wave per tensor per tile
-  using SM = SplitSmem<D, NS>;
+  using SM = SplitSmem<D, NS, NB>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[SM::HALVES];
 
   // ---- workgroup -> (batch, head, unit), XCD-aware as in fa_fwd_kernel ----
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(NS * 64) void fa_fwd_split_kernel(const FwdArgs a) 
   const int t_begin = w * tps;
   const int t_end = min(ntiles, t_begin + tps);
 
-  uint16_t* wl = smem + w * SM::WAVE;  // this wave's LDS: K0 K1 V0 V1
+  uint16_t* wl = smem + w * SM::WAVE;  // this wave's LDS: K buffers, then V buffers
   // DMA of tile t into buffer `buf`: chunk slot P = 64 i + lane of the tile
   // is row P / CPR, slot P % CPR, and receives that row's chunk
   // (slot ^ swizzle); rows past kv_end lie outside the descriptor and arrive
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(NS * 64) void fa_fwd_split_kernel(const FwdArgs a) 
         (void*)(Vg + (int64_t)t * BC * a.v_sr), (short)0, (int)((rows - 1) * (a.v_sr * 2) + D * 2),
         kBufferDword3);
     uint16_t* kd = wl + buf * SM::TILE;
-    uint16_t* vd = wl + (2 + buf) * SM::TILE;
+    uint16_t* vd = wl + (NB + buf) * SM::TILE;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int P = 64 * i + lane;
@@ -137,8 +137,8 @@ __global__ __launch_bounds__(NS * 64) void fa_fwd_split_kernel(const FwdArgs a) 
   if (t_begin < t_end) {
     dma(t_begin, 0);
     for (int t = t_begin; t < t_end; ++t) {
-      const int buf = (t - t_begin) & 1;
-      if (t + 1 < t_end) {
+      const int buf = NB == 2 ? (t - t_begin) & 1 : 0;
+      if (NB == 2 && t + 1 < t_end) {
         dma(t + 1, buf ^ 1);
         wait_vmcnt<2 * LOADS>();  // tile t has landed; tile t+1 may be in flight
       } else {
@@ -147,8 +147,11 @@ __global__ __launch_bounds__(NS * 64) void fa_fwd_split_kernel(const FwdArgs a) 
       const int key0 = t * BC;
       const bool need_mask = (key0 + BC > Nb) || (CAUSAL && key0 + BC - 1 > qw0);
       tile_step_fwd<D, DT, CAUSAL, 1, BC, 0, 0, PF>(t == t_begin, need_mask, wl + buf * SM::TILE,
-                                                    wl + (2 + buf) * SM::TILE, key0, Nb, qw0, lane, a.c, qf,
+                                                    wl + (NB + buf) * SM::TILE, key0, Nb, qw0, lane, a.c, qf,
                                                     oacc, m_run, l_run);
+      // one buffer: the next tile's loads wait until this tile's LDS reads
+      // are done (the MFMAs that consumed them have been issued)
+      if (NB == 1 && t + 1 < t_end) dma(t + 1, 0);
     }
   }
 

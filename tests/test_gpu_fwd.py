@@ -57,17 +57,19 @@ def test_workload_parity(name, seed):
     say(f"  {name} seed {seed}: max|dO| {eo:.3e}  max|dLSE| {el:.3e}")
 
 
-# The d=64 dispatch switches from the key-split kernel (one workgroup per
-# 32-row unit, keys split over 4 waves) to the main kernel when
-# B*H*ceil(N/128) passes 128. Both sides of the boundary, against the oracle;
-# a few long rows split over the waves with large logits (rescale in the
-# merge), and sequences whose tiles leave some waves without keys.
-@pytest.mark.parametrize("H,N,dtype,causal", [(128, 128, "f16", False), (129, 128, "bf16", True),
-                                              (2, 4096, "bf16", False), (1, 3000, "f16", True),
-                                              (3, 100, "bf16", True), (4, 192, "f16", False)])
-def test_key_split_path(H, N, dtype, causal):
+# The dispatch runs the key-split kernel (one workgroup per 32-row unit, keys
+# split over 4 waves) while B*H*ceil(N/32) is at most 512 (d=64) or 256
+# (d=128), and the main kernel past that. Both sides of each boundary,
+# against the oracle; long rows split over the waves with large logits
+# (rescales in the merge), and short sequences that leave waves without keys.
+@pytest.mark.parametrize("H,N,d,dtype,causal", [
+    (32, 512, 64, "f16", False), (32, 513, 64, "bf16", True),
+    (8, 1024, 128, "bf16", False), (8, 1025, 128, "f16", True),
+    (2, 4096, 64, "bf16", False), (1, 3000, 64, "f16", True), (2, 4096, 128, "bf16", True),
+    (3, 100, 64, "bf16", True), (4, 192, 128, "f16", False)])
+def test_key_split_path(H, N, d, dtype, causal):
     rows = P.sample_rows(1, H, N, 300, H + N) if H * N * N > 4 * 1024 * 1024 else None
-    run_case(1, H, N, 64, dtype, causal, 40 + H, None, 2.5, 1.0, rows)
+    run_case(1, H, N, d, dtype, causal, 40 + H, None, 2.5, 1.0, rows)
 
 
 def test_long_causal_variance3_reading():
