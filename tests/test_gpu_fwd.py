@@ -332,3 +332,30 @@ def test_varlen(causal, d, dtype):
         ro, rl = oracle.attention_fwd(t(qd), t(kd), t(vd), d ** -0.5, causal)
         P.gate_o(og[sl].transpose(1, 0, 2)[None], ro, dtype, what=f"O seq {b}")
         P.gate_lse(lg[:, sl][None], rl)
+
+
+# ---------------------------------------------------------------------------
+# beyond 2^31 elements per tensor: every offset must be 64-bit
+# ---------------------------------------------------------------------------
+def test_tensors_beyond_2pow31_elements():
+    B, H, N, d = 256, 130, 1024, 64  # 2.18e9 elements, 4.4 GB per tensor
+    assert B * H * N * d > 2 ** 31
+    say(f"[fa_fwd + fa_bwd] B{B} H{H} N{N} d{d} f16 ({B * H * N * d} elements per tensor)")
+    g = torch.Generator(device=DEV).manual_seed(123)
+    q, k, v, do = (torch.randn((B, H, N, d), generator=g, device=DEV, dtype=torch.float16) for _ in range(4))
+    o, lse = fa.attention(q, k, v)
+    # heads at the start, middle and end; the last ones lie wholly past 2^31 elements
+    heads = [(0, 0), (B // 2, 7), (B - 1, H - 2), (B - 1, H - 1)]
+    for b, h in heads:
+        qh, kh, vh = (P.decode(x[b, h][None, None].cpu(), "f16") for x in (q, k, v))
+        ro, rl = oracle.attention_fwd(qh, kh, vh, d ** -0.5, False)
+        P.gate_o(P.to64(o[b, h][None, None]), ro, "f16", what=f"O head ({b},{h})")
+        P.gate_lse(P.to64(lse[b, h][None, None]), rl)
+    dq, dk, dv = fa.attention_backward(q, k, v, o, lse, do)
+    torch.cuda.synchronize()
+    b, h = B - 1, H - 1
+    qh, kh, vh, doh = (P.decode(x[b, h][None, None].cpu(), "f16") for x in (q, k, v, do))
+    refs = oracle.attention_bwd(qh, kh, vh, doh, d ** -0.5, False)
+    for name, gpu, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
+        err = np.abs(P.to64(gpu[b, h][None, None]) - ref).max()
+        assert err <= 8 * 2.0 ** -11 * np.abs(ref).max() + 2.0 ** -11, (name, err)
