@@ -25,7 +25,7 @@
 //  * The reference m of a row is its first tile's max. Later tiles skip the
 //    max entirely: their weights p = exp2(s*c - m) are formed with the
 //    standing m and only their partial sums are checked; a tile whose
-//    partial sums reach kPartialCap (so some weight could leave the 16-bit
+//    partial sums reach partial_cap (so some weight could leave the 16-bit
 //    range) is redone with the true max and a rescale of the output
 //    accumulator. O = acc / l and LSE = (m + log2 l) ln 2 are exact for any
 //    reference m, so only the range of p matters, not which m is used.
@@ -66,9 +66,17 @@ struct FwdArgs {
 };
 
 // A weight tile is accepted when each lane's partial sums of its 16-bit
-// weights (at most 8 weights each) stay below this: every weight is then below
-// 2^15, inside the fp16 range, and the fp32 sums cannot overflow.
-constexpr float kPartialCap = 32768.0f;
+// weights (at most 8 weights each) stay below this cap. fp16: every weight is
+// then below 2^15, inside the fp16 range. bf16 weights keep their relative
+// precision at any magnitude, so their cap is 2^32: a row's sum then grows by
+// less than 2^35 per 64-key tile and stays below 2^60 even for 2^31 keys, and
+// the unnormalised output stays finite for |v| < 2^67. A redo then needs a
+// score 32 (log2) units above the row's reference, which large-logit inputs
+// rarely reach.
+template <int DT>
+constexpr float partial_cap() {
+  return DT == DT_BF16 ? 4294967296.0f : 32768.0f;
+}
 
 // dword 3 of a raw buffer descriptor on gfx950 (32-bit data format, raw
 // addressing; loads past num_records return zero)
@@ -236,7 +244,7 @@ __device__ __forceinline__ void tile_step_fwd(bool first, bool masked, const uin
     if (first) m_run[j] = tile_max();
     probs(m_run[j] == -INFINITY ? 0.f : m_run[j]);
     const float pk = fmaxf(fmaxf(lp[0], lp[1]), fmaxf(lp[2], lp[3]));
-    if (wave_any(!(pk < kPartialCap))) {
+    if (wave_any(!(pk < partial_cap<DT>()))) {
       // some weight may have left the 16-bit range: raise the reference to
       // the true max, rescale what has been accumulated, redo the weights
       // (through an offset the compiler cannot see is zero, so that K and
