@@ -176,6 +176,29 @@ def test_dominant_score_selects_row():
     P.gate_o(P.to64(o[0, 0]), ref, "f16")
 
 
+@pytest.mark.parametrize("jump", [18.0, 40.0])
+def test_bf16_late_dominant_key(jump):
+    # One late key scores `jump` (natural-log units) above every other key, so
+    # its weight relative to the first tile's reference is about 2^(1.44 jump):
+    # 2^26 at 18 (accepted under the 2^32 bf16 cap, no redo) and 2^58 at 40
+    # (a redo and a rescale). Either way O and LSE must match the oracle.
+    say(f"[bf16] late dominant key, jump {jump}")
+    N, d, sc = 1000, 64, 0.125
+    g = torch.Generator().manual_seed(11)
+    q = torch.zeros(1, 2, N, d)
+    q[..., 0] = 1.0
+    k = torch.randn(1, 2, N, d, generator=g) * 0.05
+    k[0, :, 900] = 0.0
+    k[0, :, 900, 0] = jump / sc
+    v = torch.randn(1, 2, N, d, generator=g)
+    q, k, v = q.bfloat16(), k.bfloat16(), v.bfloat16()
+    o, lse = _gpu(q, k, v, False, sc)
+    qd, kd, vd = (P.decode(x, "bf16") for x in (q, k, v))
+    ro, rl = oracle.attention_fwd(qd, kd, vd, sc, False)
+    P.gate_o(P.to64(o), ro, "bf16")
+    P.gate_lse(P.to64(lse), rl)
+
+
 def test_deterministic():
     q, k, v = (t.to(DEV) for t in inputs.make_qkv(2, 4, 1000, 64, "f16", 51))
     o1, l1 = fa.attention(q, k, v, causal=True)
