@@ -7,7 +7,7 @@
 //   dK = scale · dSᵀ Q,  dQ = scale · dS K.
 //
 // MI355X layout (our design): three kernels (the dK/dV one as two passes,
-// dV then dK, at d = 96 and 128) and no atomics.
+// dV then dK, at d = 96) and no atomics.
 //  * fa_bwd_dot_kernel: D_i in fp32.
 //  * fa_bwd_dkdv_kernel: one workgroup per block of 128 keys, each wave owning
 //    32 keys whose K and V fragments stay in registers; 64-query tiles of Q,
@@ -15,10 +15,13 @@
 //    the lane (S = Q Kᵀ), so P and dS are directly the B operand of
 //    dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS, whose A operands (dOᵀ, Qᵀ) come from the
 //    row-major LDS tiles through the transposing LDS read.
+//  * fa_bwd_dkdv_wide_kernel (d = 128): the same in one pass, 256 keys per
+//    workgroup, V fragments parked in LDS and Q/dO tiles by LDS-DMA.
 //  * fa_bwd_dq_kernel: the mirror image with the query in the lane (like the
 //    forward): Pᵀ = exp2(Sᵀ c - LSE log2 e), dPᵀ = V dOᵀ, dQᵀ += Kᵀ dSᵀ.
 #pragma once
 #include "fa_fwd_kernel.h"
+#include "fa_fwd_split.h"
 
 namespace fa {
 
@@ -298,6 +301,215 @@ __global__ __launch_bounds__(256, PART == BWD_DKDV ? 1 : 2) void fa_bwd_dkdv_ker
           y[1] = pack2<DT>(dv[db][4 * g4 + 2], dv[db][4 * g4 + 3]);
           *(u32x2*)(dvr + col) = y;
         }
+      }
+  }
+}
+
+// ---- dK and dV in one pass at d = 128: 8 waves, 256 keys ----
+// The mathematics of fa_bwd_dkdv_kernel with both accumulators, so S and the
+// exponentials are computed once per (query, key) pair instead of once per
+// pass. What makes both accumulators fit two waves per SIMD:
+//  * each wave keeps only its K fragments in registers and parks its V
+//    fragments in its own LDS slice, in fragment order (one conflict-free
+//    16-byte read per lane and k-step);
+//  * the 64-query Q and dO tiles arrive by LDS-DMA (buffer_load ... lds, no
+//    staging registers) into unpadded rows whose 16-byte chunks are
+//    XOR-swizzled (lds_off<D, 0>), double-buffered and shared by the 8 waves.
+// A negative scale flips the sign of K (so S keeps the sign of scale·q·k)
+// and multiplies dK at the end; Q is used as stored.
+template <int D, int DT, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_wide_kernel(const BwdArgs a) {
+  constexpr int NW = 8, KK = D / 16, DB = D / 32, KW = 32 * NW, BQ = 64, CPR = D / 8;
+  constexpr int TILE = BQ * D;                   // halves per unpadded Q or dO tile
+  constexpr int STAGE = 2 * TILE + 2 * BQ * 2;   // Q, dO, then the row terms (fp32)
+  constexpr int LOADS = BQ * CPR / 64;           // wave loads (1 KB) per tensor per tile
+  static_assert(LOADS % NW == 0, "tile loads split evenly over the waves");
+  constexpr int LPW = LOADS / NW;
+  constexpr int VFRAG = KK * 64;                 // u32x4 per wave
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE + NW * VFRAG * 8];
+
+  const int nkb = (a.N + KW - 1) / KW;
+  const int bh = blockIdx.x / nkb, kblk = blockIdx.x - bh * nkb;
+  if (bh >= a.B * a.H) return;
+  const int64_t off = (int64_t)bh * a.N * D;
+  const uint16_t* Qg = a.q + off;
+  const uint16_t* Kg = a.k + off;
+  const uint16_t* Vg = a.v + off;
+  const uint16_t* Gg = a.dout + off;
+  const float* Lg = a.lse + (int64_t)bh * a.N;
+  const float* Dg = a.dvec + (int64_t)bh * a.N;
+  const int N = a.N;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int kw0 = kblk * KW + w * 32;  // first key of this wave
+  const int krow = kw0 + l32;
+
+  // K fragments (sign of the scale folded in) in registers, V fragments in
+  // this wave's LDS slice; keys past the end are zero
+  u32x4 kf[KK];
+  u32x4* vl = (u32x4*)(smem + 2 * STAGE) + w * VFRAG;
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const int rr = min(krow, N - 1);
+    const u32x4 xk = *(const u32x4*)(Kg + (int64_t)rr * D + 16 * kk + 8 * hh);
+    const u32x4 xv = *(const u32x4*)(Vg + (int64_t)rr * D + 16 * kk + 8 * hh);
+    kf[kk] = krow < N ? (xk ^ a.qsign) : u32x4{0u, 0u, 0u, 0u};
+    vl[kk * 64 + lane] = krow < N ? xv : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[db][r] = 0.f;
+      dv[db][r] = 0.f;
+    }
+
+  // query tiles: causal blocks start at the tile holding the block's first key
+  const int t0 = CAUSAL ? (kblk * KW) / BQ : 0;
+  const int nt = (N + BQ - 1) / BQ;
+
+  // this wave's share of the Q and dO tiles of query tile t: chunk slot
+  // P = 64 i + lane is row P / CPR, slot P % CPR, and receives that row's
+  // chunk (slot ^ swizzle); rows past the end lie outside the descriptor and
+  // arrive as zeros
+  auto dma = [&](int t, int buf) __attribute__((always_inline)) {
+    const int q0 = t * BQ;
+    const int rows = min(N - q0, BQ);  // >= 1
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Qg + (int64_t)q0 * D), (short)0, rows * D * 2, kBufferDword3);
+    const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Gg + (int64_t)q0 * D), (short)0, rows * D * 2, kBufferDword3);
+    uint16_t* dq = smem + buf * STAGE;
+    uint16_t* dg = dq + TILE;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int i = w * LPW + j;
+      const int P = 64 * i + lane;
+      const int r = P / CPR, ch = (P % CPR) ^ lds_swz<D>(r);
+      const uint32_t o = (uint32_t)(r * D * 2 + ch * 16);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void*)(dq + 64 * i * 8), 16,
+                                               o, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, (__attribute__((address_space(3))) void*)(dg + 64 * i * 8), 16,
+                                               o, 0, 0, 0);
+    }
+  };
+  // per query row: -LSE log2(e) / c and -D_i, the starting values of the S
+  // and dP accumulators (rows past the end: -inf, so their weights are zero)
+  float ls = 0.f, ds = 0.f;
+  const float inv_c = 1.f / a.c;
+  auto fetch_rows = [&](int t) __attribute__((always_inline)) {
+    if (tid < BQ) {
+      const int gr = t * BQ + tid;
+      ls = gr < N ? -Lg[gr] * kLog2e * inv_c : -INFINITY;
+      ds = gr < N ? -Dg[gr] : 0.f;
+    }
+  };
+  auto stash_rows = [&](int buf) __attribute__((always_inline)) {
+    float* sl = (float*)(smem + buf * STAGE + 2 * TILE);
+    if (tid < BQ) {
+      sl[tid] = ls;
+      sl[BQ + tid] = ds;
+    }
+  };
+
+  if (t0 < nt) {
+    dma(t0, 0);
+    fetch_rows(t0);
+    stash_rows(0);
+  }
+  const int g16 = lane >> 4, s16 = lane & 15;
+  for (int t = t0; t < nt; ++t) {
+    // tile t has landed (this wave's DMA, then everyone's), its row terms
+    // are stored, and no wave still reads the other buffer
+    wait_vmcnt<0>();
+    __syncthreads();
+    const int buf = (t - t0) & 1;
+    if (t + 1 < nt) {
+      dma(t + 1, buf ^ 1);
+      fetch_rows(t + 1);
+    }
+    const uint16_t* sq = smem + buf * STAGE;
+    const uint16_t* sg = sq + TILE;
+    const float* sl = (const float*)(sg + TILE);
+    const int q0 = t * BQ;
+#pragma unroll 1
+    for (int qb = 0; qb < BQ / 32; ++qb) {
+      const int qr0 = q0 + 32 * qb;
+      if (CAUSAL && qr0 + 31 < kw0) continue;  // every query precedes every key
+      f32x16 s = load_rowvals(sl + 32 * qb, hh), dp = load_rowvals(sl + BQ + 32 * qb, hh);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const u32x4 qa = *(const u32x4*)(sq + lds_off<D, 0>(32 * qb + l32, 16 * kk + 8 * hh));
+        const u32x4 ga = *(const u32x4*)(sg + lds_off<D, 0>(32 * qb + l32, 16 * kk + 8 * hh));
+        s = mfma32x32x16<DT>(qa, kf[kk], s);
+        dp = mfma32x32x16<DT>(ga, vl[kk * 64 + lane], dp);
+      }
+      // phase boundaries for the scheduler: LDS reads hoisted across them
+      // would hold registers through the exponentials (48 spilled)
+      __builtin_amdgcn_sched_barrier(0);
+      const bool diag = CAUSAL && qr0 < kw0 + 31;
+      u32x4 pp[2], sp[2];
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float pv[2], sv[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int r = 8 * c2 + 2 * e + u;
+            float p = fast_exp2(s[r] * a.c);
+            if (CAUSAL && diag) {
+              const int qrow = qr0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+              if (krow > qrow) p = 0.f;
+            }
+            pv[u] = p;
+            sv[u] = p * dp[r];
+          }
+          pp[c2][e] = pack2<DT>(pv[0], pv[1]);
+          sp[c2][e] = pack2<DT>(sv[0], sv[1]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS ; k-slot 8*hh + 4*rd + e of chunk c2 is
+      // query 16*c2 + 8*rd + 4*hh + e of this block
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const int ra = 32 * qb + 16 * c2 + 4 * hh + (s16 >> 2);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int col = db * 32 + (g16 & 1) * 16 + 4 * (s16 & 3);
+          const u32x2 glo = lds_read_tr4(sg + lds_off<D, 0>(ra, col));
+          const u32x2 ghi = lds_read_tr4(sg + lds_off<D, 0>(ra + 8, col));
+          dv[db] = mfma32x32x16<DT>(u32x4{glo[0], glo[1], ghi[0], ghi[1]}, pp[c2], dv[db]);
+          const u32x2 qlo = lds_read_tr4(sq + lds_off<D, 0>(ra, col));
+          const u32x2 qhi = lds_read_tr4(sq + lds_off<D, 0>(ra + 8, col));
+          dk[db] = mfma32x32x16<DT>(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, sp[c2], dk[db]);
+        }
+      }
+    }
+    if (t + 1 < nt) stash_rows(buf ^ 1);
+  }
+
+  // dK = scale dSᵀ Q, dV = Pᵀ dO; key row, 4 consecutive d per group
+  if (krow < N) {
+    uint16_t* dkr = a.dk + off + (int64_t)krow * D;
+    uint16_t* dvr = a.dv + off + (int64_t)krow * D;
+    const float sk = a.scale;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int col = db * 32 + 8 * g4 + 4 * hh;
+        u32x2 x, y;
+        x[0] = pack2<DT>(dk[db][4 * g4 + 0] * sk, dk[db][4 * g4 + 1] * sk);
+        x[1] = pack2<DT>(dk[db][4 * g4 + 2] * sk, dk[db][4 * g4 + 3] * sk);
+        y[0] = pack2<DT>(dv[db][4 * g4 + 0], dv[db][4 * g4 + 1]);
+        y[1] = pack2<DT>(dv[db][4 * g4 + 2], dv[db][4 * g4 + 3]);
+        *(u32x2*)(dkr + col) = x;
+        *(u32x2*)(dvr + col) = y;
       }
   }
 }

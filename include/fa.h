@@ -132,8 +132,8 @@ int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *l
  *                     are ignored. It holds the fp32 row terms D_i = <dO_i, O_i>.
  * Head dims 64, 96 and 128 (d = 256 returns FA_ERR_UNSUPPORTED). The kernels
  * enqueued on `stream` are D_i, then dK/dV (parallel over key blocks; at
- * d = 96 and 128 two passes, dV then dK), then dQ (parallel over query
- * blocks). There are no atomics, so results are deterministic.
+ * d = 96 two passes, dV then dK), then dQ (parallel over query blocks).
+ * There are no atomics, so results are deterministic.
  */
 int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *do_,
            const float *lse, void *dq, void *dk, void *dv, void *workspace,

@@ -66,6 +66,13 @@ def test_bwd_scale_variants():
     run(1, 2, 150, 64, "bf16", True, seed=8, scale=0.3, sigma_qk=2.0)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_d128_negative_scale(causal):
+    # d = 128 folds the sign of the scale into K and into dK's final multiply
+    run(1, 2, 300, 128, "bf16", causal, seed=11, scale=-0.09)
+    run(1, 1, 513, 128, "f16", causal, seed=12, scale=-0.2)
+
+
 def test_bwd_deterministic():
     q, k, v = (t.cuda() for t in inputs.make_qkv(1, 4, 500, 64, "bf16", 9))
     do = inputs.make_like(q.cpu(), 10).cuda()
