@@ -14,11 +14,14 @@ int64_t bwd_bytes(int B, int H, int N) {
   return ((int64_t)B * H * N * 4 + 255) / 256 * 256;  // D_i in fp32
 }
 
-// d = 128: dK and dV in one pass of 8-wave, 256-key blocks (V fragments in
-// LDS), and 8-wave dQ blocks; d = 96: dV and dK in two passes; d = 64: one
-// pass. Every kernel runs two waves per SIMD. N=8192 causal bf16 d=128:
-// 3563 us per backward against 4610 us with two passes (dV 1331 us, dK
-// 1596 us); B4 H16 N4096 fp16: 2125 us against 2833 us.
+// dK and dV in one pass with V fragments in LDS: d = 128 in 8-wave, 256-key
+// blocks (two waves per SIMD; with 8-wave dQ blocks), d = 64 in 4-wave,
+// 128-key blocks (three waves per SIMD); d = 96 in two passes. Against the
+// earlier two passes (d = 128) and fused 4-wave kernel with K and V
+// fragments in registers (d = 64, two waves per SIMD), per backward:
+// N=8192 causal bf16 d=128 3563 vs 4610 us, B4 H16 N4096 fp16 d=128 2125 vs
+// 2833 us, B4 H16 N4096 fp16 d=64 1131 vs 1203 us, N=400 x128 heads bf16
+// 52.9 vs 54.1 us.
 template <int D, int DT, bool CAUSAL>
 int launch(const BwdArgs& a, hipStream_t st) {
   constexpr int QNW = D == 128 ? 8 : 4;
@@ -32,12 +35,12 @@ int launch(const BwdArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((fa_bwd_dot_kernel<D, DT>), dim3((unsigned)gdot), dim3(256), 0, st, a);
   if constexpr (D == 128) {
     const int64_t gw = (int64_t)a.B * a.H * ((a.N + 255) / 256);
-    hipLaunchKernelGGL((fa_bwd_dkdv_wide_kernel<D, DT, CAUSAL>), dim3((unsigned)gw), dim3(512), 0, st, a);
+    hipLaunchKernelGGL((fa_bwd_dkdv_wide_kernel<D, DT, CAUSAL, 8, 1>), dim3((unsigned)gw), dim3(512), 0, st, a);
   } else if constexpr (D == 96) {
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, DT, CAUSAL, BWD_DV>), dim3((unsigned)gk), dim3(256), 0, st, a);
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, DT, CAUSAL, BWD_DK>), dim3((unsigned)gk), dim3(256), 0, st, a);
   } else {
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, DT, CAUSAL, BWD_DKDV>), dim3((unsigned)gk), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((fa_bwd_dkdv_wide_kernel<D, DT, CAUSAL, 4, 3>), dim3((unsigned)gk), dim3(256), 0, st, a);
   }
   hipLaunchKernelGGL((fa_bwd_dq_kernel<D, DT, CAUSAL, QNW>), dim3((unsigned)gq), dim3(QNW * 64), 0, st, a);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;

@@ -6,17 +6,16 @@
 //   dV = Pᵀ dO,  dS = P ∘ (dP - D),  D_i = <dO_i, O_i>,
 //   dK = scale · dSᵀ Q,  dQ = scale · dS K.
 //
-// MI355X layout (our design): three kernels (the dK/dV one as two passes,
-// dV then dK, at d = 96) and no atomics.
+// MI355X layout (our design): three kernels and no atomics.
 //  * fa_bwd_dot_kernel: D_i in fp32.
-//  * fa_bwd_dkdv_kernel: one workgroup per block of 128 keys, each wave owning
-//    32 keys whose K and V fragments stay in registers; 64-query tiles of Q,
-//    dO, LSE and D stream through LDS. S and dP are computed with the key in
-//    the lane (S = Q Kᵀ), so P and dS are directly the B operand of
-//    dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS, whose A operands (dOᵀ, Qᵀ) come from the
-//    row-major LDS tiles through the transposing LDS read.
-//  * fa_bwd_dkdv_wide_kernel (d = 128): the same in one pass, 256 keys per
-//    workgroup, V fragments parked in LDS and Q/dO tiles by LDS-DMA.
+//  * fa_bwd_dkdv_wide_kernel (d = 64, 128): one workgroup per block of keys,
+//    each wave owning 32 keys; 64-query tiles of Q, dO, LSE and D stream
+//    through LDS. S and dP are computed with the key in the lane (S = Q Kᵀ),
+//    so P and dS are directly the B operand of dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS,
+//    whose A operands (dOᵀ, Qᵀ) come from the row-major LDS tiles through the
+//    transposing LDS read.
+//  * fa_bwd_dkdv_kernel (d = 96): the same as two passes, dV then dK, with
+//    K and V fragments in registers.
 //  * fa_bwd_dq_kernel: the mirror image with the query in the lane (like the
 //    forward): Pᵀ = exp2(Sᵀ c - LSE log2 e), dPᵀ = V dOᵀ, dQᵀ += Kᵀ dSᵀ.
 #pragma once
@@ -103,15 +102,16 @@ __device__ __forceinline__ f32x16 load_rowvals(const float* base, int hh) {
   return v;
 }
 
-// ---- dK, dV: one workgroup per 128 keys ----
-// PART 0 computes both; PART 1 only dV (no V fragments, no dP) and PART 2
-// only dK. At d = 128 the two halves run as separate passes: each then fits
-// two waves per SIMD, where both together hold one (the K and V fragments
-// and both accumulators alone take 192 registers per lane).
-enum { BWD_DKDV = 0, BWD_DV = 1, BWD_DK = 2 };
+// ---- dK, dV in two passes: one workgroup per 128 keys ----
+// PART BWD_DV computes only dV (no V fragments, no dP), PART BWD_DK only dK.
+// Each pass then fits two waves per SIMD with the K and V fragments in
+// registers (d = 96, whose 12 chunks per row do not split over the
+// single-pass kernel's LDS-DMA).
+enum { BWD_DV = 1, BWD_DK = 2 };
 template <int D, int DT, bool CAUSAL, int PART>
-__global__ __launch_bounds__(256, PART == BWD_DKDV ? 1 : 2) void fa_bwd_dkdv_kernel(const BwdArgs a) {
-  constexpr bool WANT_DV = PART != BWD_DK, WANT_DK = PART != BWD_DV;
+__global__ __launch_bounds__(256, 2) void fa_bwd_dkdv_kernel(const BwdArgs a) {
+  static_assert(PART == BWD_DV || PART == BWD_DK, "one of the two passes");
+  constexpr bool WANT_DV = PART == BWD_DV, WANT_DK = PART == BWD_DK;
   constexpr int NW = 4, NT = 256, KK = D / 16, DB = D / 32;
   using SM = BwdSmem<D>;
   constexpr int BQ = SM::BQ, STR = SM::STR;
@@ -305,21 +305,21 @@ __global__ __launch_bounds__(256, PART == BWD_DKDV ? 1 : 2) void fa_bwd_dkdv_ker
   }
 }
 
-// ---- dK and dV in one pass at d = 128: 8 waves, 256 keys ----
-// The mathematics of fa_bwd_dkdv_kernel with both accumulators, so S and the
-// exponentials are computed once per (query, key) pair instead of once per
-// pass. What makes both accumulators fit two waves per SIMD:
+// ---- dK and dV in one pass: NW waves, 32 NW keys per workgroup ----
+// Both accumulators in one pass, so S and the exponentials are computed once
+// per (query, key) pair. What keeps the registers down (d = 128, 8 waves:
+// two waves per SIMD; d = 64, 4 waves: three):
 //  * each wave keeps only its K fragments in registers and parks its V
 //    fragments in its own LDS slice, in fragment order (one conflict-free
 //    16-byte read per lane and k-step);
 //  * the 64-query Q and dO tiles arrive by LDS-DMA (buffer_load ... lds, no
 //    staging registers) into unpadded rows whose 16-byte chunks are
-//    XOR-swizzled (lds_off<D, 0>), double-buffered and shared by the 8 waves.
+//    XOR-swizzled (lds_off<D, 0>), double-buffered and shared by the NW waves.
 // A negative scale flips the sign of K (so S keeps the sign of scale·q·k)
 // and multiplies dK at the end; Q is used as stored.
-template <int D, int DT, bool CAUSAL>
-__global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_wide_kernel(const BwdArgs a) {
-  constexpr int NW = 8, KK = D / 16, DB = D / 32, KW = 32 * NW, BQ = 64, CPR = D / 8;
+template <int D, int DT, bool CAUSAL, int NW, int MINB>
+__global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv_wide_kernel(const BwdArgs a) {
+  constexpr int KK = D / 16, DB = D / 32, KW = 32 * NW, BQ = 64, CPR = D / 8;
   constexpr int TILE = BQ * D;                   // halves per unpadded Q or dO tile
   constexpr int STAGE = 2 * TILE + 2 * BQ * 2;   // Q, dO, then the row terms (fp32)
   constexpr int LOADS = BQ * CPR / 64;           // wave loads (1 KB) per tensor per tile
