@@ -21,7 +21,9 @@ int64_t bwd_bytes(int B, int H, int N) {
 // fragments in registers (d = 64, two waves per SIMD), per backward:
 // N=8192 causal bf16 d=128 3563 vs 4610 us, B4 H16 N4096 fp16 d=128 2125 vs
 // 2833 us, B4 H16 N4096 fp16 d=64 1131 vs 1203 us, N=400 x128 heads bf16
-// 52.9 vs 54.1 us.
+// 52.9 vs 54.1 us. The dQ kernel with K/V by LDS-DMA (and, at d = 64, dO
+// fragments in LDS: three waves per SIMD) then took these to 3216, 1015 and
+// 49.5 us (N=8192 causal, N=4096 d=64, N=400) from 3562, 1097 and 52.2.
 template <int D, int DT, bool CAUSAL>
 int launch(const BwdArgs& a, hipStream_t st) {
   constexpr int QNW = D == 128 ? 8 : 4;
@@ -42,7 +44,10 @@ int launch(const BwdArgs& a, hipStream_t st) {
   } else {
     hipLaunchKernelGGL((fa_bwd_dkdv_wide_kernel<D, DT, CAUSAL, 4, 3>), dim3((unsigned)gk), dim3(256), 0, st, a);
   }
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, DT, CAUSAL, QNW>), dim3((unsigned)gq), dim3(QNW * 64), 0, st, a);
+  if constexpr (D == 96)
+    hipLaunchKernelGGL((fa_bwd_dq_staged_kernel<D, DT, CAUSAL, QNW>), dim3((unsigned)gq), dim3(QNW * 64), 0, st, a);
+  else
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, DT, CAUSAL, QNW>), dim3((unsigned)gq), dim3(QNW * 64), 0, st, a);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

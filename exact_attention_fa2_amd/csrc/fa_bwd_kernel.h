@@ -16,8 +16,9 @@
 //    transposing LDS read.
 //  * fa_bwd_dkdv_kernel (d = 96): the same as two passes, dV then dK, with
 //    K and V fragments in registers.
-//  * fa_bwd_dq_kernel: the mirror image with the query in the lane (like the
-//    forward): Pᵀ = exp2(Sᵀ c - LSE log2 e), dPᵀ = V dOᵀ, dQᵀ += Kᵀ dSᵀ.
+//  * fa_bwd_dq_kernel (d = 64, 128): the mirror image with the query in the
+//    lane (like the forward): Pᵀ = exp2(Sᵀ c - LSE log2 e), dPᵀ = V dOᵀ,
+//    dQᵀ += Kᵀ dSᵀ; fa_bwd_dq_staged_kernel is the same for d = 96.
 #pragma once
 #include "fa_fwd_kernel.h"
 #include "fa_fwd_split.h"
@@ -514,11 +515,194 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv_wide_kernel(const B
   }
 }
 
-// ---- dQ: one workgroup per 128 queries (query in the lane) ----
-// NW waves of 32 query rows per workgroup (8 at d = 128: fewer staging
-// registers per thread keep it at two waves per SIMD).
+// ---- dQ: one workgroup per NW*32 queries (query in the lane) ----
+// NW waves of 32 query rows per workgroup (8 at d = 128, 4 at d = 64). K/V
+// tiles arrive by LDS-DMA into unpadded, XOR-swizzled rows (no staging
+// registers); at d = 64 each wave also parks its dO fragments in its own LDS
+// slice, which brings the kernel to three waves per SIMD.
 template <int D, int DT, bool CAUSAL, int NW>
-__global__ __launch_bounds__(NW * 64) void fa_bwd_dq_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_bwd_dq_kernel(const BwdArgs a) {
+  static_assert(D == 64 || D == 128, "swizzled LDS-DMA tiles: d = 64 or 128");
+  constexpr int BR = NW * 32, BC = 64, KK = D / 16, DB = D / 32, KB = BC / 32, CPR = D / 8;
+  constexpr int TILE = BC * D;                   // halves per unpadded K or V tile
+  constexpr int LOADS = BC * CPR / 64;           // wave loads (1 KB) per tensor per tile
+  static_assert(LOADS % NW == 0, "tile loads split evenly over the waves");
+  constexpr int LPW = LOADS / NW;
+  constexpr bool GL = D == 64;                   // dO fragments parked in LDS
+  constexpr int GFRAG = KK * 64;                 // u32x4 per wave
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE + (GL ? NW * GFRAG * 8 : 0)];
+
+  const int nqb = (a.N + BR - 1) / BR;
+  const int bh = blockIdx.x / nqb, qblk0 = blockIdx.x - bh * nqb;
+  if (bh >= a.B * a.H) return;
+  const int qblk = CAUSAL ? nqb - 1 - qblk0 : qblk0;  // longest first
+  const int64_t off = (int64_t)bh * a.N * D;
+  const uint16_t* Qg = a.q + off;
+  const uint16_t* Kg = a.k + off;
+  const uint16_t* Vg = a.v + off;
+  const uint16_t* Gg = a.dout + off;
+  const int N = a.N;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int qw0 = qblk * BR + w * 32;
+  const int qrow = qw0 + l32;
+
+  u32x4 qf[KK], gf[GL ? 1 : KK];
+  u32x4* gl = (u32x4*)(smem + 4 * TILE) + w * GFRAG;
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const int rr = min(qrow, N - 1);
+    const u32x4 x = *(const u32x4*)(Qg + (int64_t)rr * D + 16 * kk + 8 * hh);
+    const u32x4 y = *(const u32x4*)(Gg + (int64_t)rr * D + 16 * kk + 8 * hh);
+    qf[kk] = (qrow < N ? x : u32x4{0u, 0u, 0u, 0u}) ^ a.qsign;
+    const u32x4 g = qrow < N ? y : u32x4{0u, 0u, 0u, 0u};
+    if constexpr (GL)
+      gl[kk * 64 + lane] = g;
+    else
+      gf[kk] = g;
+  }
+  const float lq = qrow < N ? a.lse[(int64_t)bh * N + qrow] * kLog2e : INFINITY;
+  const float dq_row = qrow < N ? a.dvec[(int64_t)bh * N + qrow] : 0.f;
+
+  f32x16 dqacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dqacc[db][r] = 0.f;
+
+  const int kv_end = CAUSAL ? min(N, (qblk + 1) * BR) : N;
+  const int ntiles = (kv_end + BC - 1) / BC;
+  // tiles this wave computes: causal waves stop at their own diagonal (the
+  // rest are fully masked) and then only help with the loads; waves with no
+  // rows only help with the loads
+  const int wave_end = qw0 >= N ? 0 : (CAUSAL ? min(kv_end, qw0 + 32) : kv_end);
+  const int wnt = (wave_end + BC - 1) / BC;
+  // this wave's share of K/V tile t into buffer `buf`: chunk slot P = 64 i +
+  // lane is row P / CPR, slot P % CPR, and receives that row's chunk (slot ^
+  // swizzle); rows past kv_end lie outside the descriptor and arrive as zeros
+  auto dma = [&](int t, int buf) __attribute__((always_inline)) {
+    const int rows = min(kv_end - t * BC, BC);  // >= 1
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Kg + (int64_t)t * BC * D), (short)0, rows * D * 2, kBufferDword3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Vg + (int64_t)t * BC * D), (short)0, rows * D * 2, kBufferDword3);
+    uint16_t* kd = smem + buf * 2 * TILE;
+    uint16_t* vd = kd + TILE;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int i = w * LPW + j;
+      const int P = 64 * i + lane;
+      const int r = P / CPR, ch = (P % CPR) ^ lds_swz<D>(r);
+      const uint32_t o = (uint32_t)(r * D * 2 + ch * 16);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kd + 64 * i * 8), 16,
+                                               o, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vd + 64 * i * 8), 16,
+                                               o, 0, 0, 0);
+    }
+  };
+  // tile t has landed (this wave's DMA, then everyone's) and no wave still
+  // reads the buffer the next tile goes to
+  auto arrive = [&](int t) __attribute__((always_inline)) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (t + 1 < ntiles) dma(t + 1, (t + 1) & 1);
+  };
+
+  dma(0, 0);
+  const int g16 = lane >> 4, s16 = lane & 15;
+  int t = 0;
+  for (; t < wnt; ++t) {
+    arrive(t);
+    const uint16_t* sk = smem + (t & 1) * 2 * TILE;
+    const uint16_t* sv = sk + TILE;
+    const int key0 = t * BC;
+    // Sᵀ = K Qᵀ and dPᵀ - D = V dOᵀ - D: query in the lane, keys in the
+    // registers (the dP accumulators start at -D of the lane's row)
+    f32x16 s[KB], dp[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[kb][r] = -dq_row;
+    }
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 g;
+      if constexpr (GL)
+        g = gl[kk * 64 + lane];
+      else
+        g = gf[kk];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const u32x4 ka = *(const u32x4*)(sk + lds_off<D, 0>(kb * 32 + l32, 16 * kk + 8 * hh));
+        const u32x4 va = *(const u32x4*)(sv + lds_off<D, 0>(kb * 32 + l32, 16 * kk + 8 * hh));
+        s[kb] = mfma32x32x16<DT>(ka, qf[kk], s[kb]);
+        dp[kb] = mfma32x32x16<DT>(va, g, dp[kb]);
+      }
+    }
+    // phase boundaries for the scheduler (LDS reads hoisted across them
+    // would hold registers through the exponentials)
+    __builtin_amdgcn_sched_barrier(0);
+    const bool masked = key0 + BC > N || (CAUSAL && key0 + BC - 1 > qw0);
+    u32x4 sf[BC / 16];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        u32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float v2[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int r = 8 * c2 + 2 * e + u;
+            float p = fast_exp2(__builtin_fmaf(s[kb][r], a.c, -lq));
+            if (masked) {
+              const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+              if (key >= N || (CAUSAL && key > qrow)) p = 0.f;
+            }
+            v2[u] = p * dp[kb][r];
+          }
+          x[e] = pack2<DT>(v2[0], v2[1]);
+        }
+        sf[2 * kb + c2] = x;
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    // dQᵀ += Kᵀ dSᵀ ; k-slot 8*hh + 4*rd + e of chunk ci is key 16*ci + 8*rd + 4*hh + e
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int ci = 0; ci < BC / 16; ++ci) {
+        const int col = db * 32 + (g16 & 1) * 16 + 4 * (s16 & 3);
+        const int ra = 16 * ci + 4 * hh + (s16 >> 2);
+        const u32x2 lo = lds_read_tr4(sk + lds_off<D, 0>(ra, col));
+        const u32x2 hi = lds_read_tr4(sk + lds_off<D, 0>(ra + 8, col));
+        dqacc[db] = mfma32x32x16<DT>(u32x4{lo[0], lo[1], hi[0], hi[1]}, sf[ci], dqacc[db]);
+      }
+  }
+  for (; t < ntiles; ++t) arrive(t);
+
+  if (qrow < N) {
+    uint16_t* dqr = a.dq + off + (int64_t)qrow * D;
+    const float sc = a.scale;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        u32x2 x;
+        x[0] = pack2<DT>(dqacc[db][4 * g4 + 0] * sc, dqacc[db][4 * g4 + 1] * sc);
+        x[1] = pack2<DT>(dqacc[db][4 * g4 + 2] * sc, dqacc[db][4 * g4 + 3] * sc);
+        *(u32x2*)(dqr + db * 32 + 8 * g4 + 4 * hh) = x;
+      }
+  }
+}
+
+// ---- dQ at d = 96: K/V tiles staged through registers into padded rows ----
+// (96 halves per row split into 12 chunks, which the XOR swizzle of the
+// LDS-DMA layout does not cover). Otherwise as fa_bwd_dq_kernel.
+template <int D, int DT, bool CAUSAL, int NW>
+__global__ __launch_bounds__(NW * 64) void fa_bwd_dq_staged_kernel(const BwdArgs a) {
   constexpr int NT = NW * 64, BR = NW * 32, BC = 64, KK = D / 16, DB = D / 32, KB = BC / 32;
   constexpr int CH = BC * D / 8 / NT;
   static_assert(BC * D / 8 % NT == 0, "tile must split evenly");
