@@ -81,3 +81,31 @@ def test_bwd_deterministic():
     g2 = fa.attention_backward(q, k, v, o, lse, do, causal=True)
     torch.cuda.synchronize()
     assert all(torch.equal(x, y) for x, y in zip(g1, g2))
+
+
+@pytest.mark.parametrize("name", ["n400_batched", "n4096", "n8192_causal"])
+def test_bwd_workload_sampled_heads(name):
+    # the backward at the benchmarked size, launched exactly as bench.py times
+    # it; whole (batch, head) slices compared with the oracle (first, last and
+    # one seeded head)
+    w = inputs.WORKLOADS[name]
+    print(f"[fa_bwd] workload {name}: B{w.B} H{w.H} N{w.N} d{w.d} {w.dtype} causal={w.causal}", flush=True)
+    q, k, v = inputs.make_qkv(w.B, w.H, w.N, w.d, w.dtype, 0, w.sigma_qk, w.sigma_v)
+    do = inputs.make_like(q, 1000)
+    qg, kg, vg, dog = (t.cuda() for t in (q, k, v, do))
+    o, lse = fa.attention(qg, kg, vg, causal=w.causal, scale=w.scale)
+    dq, dk, dv = fa.attention_backward(qg, kg, vg, o, lse, dog, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    grads = [P.to64(g) for g in (dq, dk, dv)]
+    assert all(np.isfinite(g).all() for g in grads)
+    rng = np.random.default_rng(7)
+    heads = {(0, 0), (w.B - 1, w.H - 1), (int(rng.integers(w.B)), int(rng.integers(w.H)))}
+    for b, h in sorted(heads):
+        qd, kd, vd, dod = (P.decode(x[b:b + 1, h:h + 1], w.dtype) for x in (q, k, v, do))
+        refs = oracle.attention_bwd(qd, kd, vd, dod, w.scale, w.causal)
+        amax = lambda x: float(np.abs(x).max())
+        floor = 2.0 ** -20 * w.d * amax(dod) * amax(vd) * w.d * max(amax(qd), amax(kd)) * abs(w.scale)
+        rel = {}
+        for gname, g, r in zip(("dq", "dk", "dv"), grads, refs):
+            rel[gname] = gate_grad(g[b:b + 1, h:h + 1], r, w.dtype, f"{gname} head ({b},{h})", floor)
+        print(f"  head ({b},{h}) rel errors", {k2: f"{v2:.2e}" for k2, v2 in rel.items()}, flush=True)
