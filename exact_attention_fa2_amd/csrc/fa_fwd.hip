@@ -26,7 +26,11 @@ int launch_one(FwdArgs a, hipStream_t st) {
 }
 
 // Key-split kernel: one workgroup of NS waves per 32-row unit, the unit's
-// keys split over the waves.
+// keys split over the waves. Against 4 waves, 8 waves per unit at d=64
+// (same box): N=2048 x4 heads 15.9 vs 19.9 us, N=4096 x2 heads causal 23.4
+// vs 30.8 us, N=8192 x1 head 39.2 vs 56.7 us; but N=400 x4 heads 8.7 vs
+// 8.1 us (7 tiles a row: one per wave, eight partials to merge) and N=400 x32
+// heads 16.4 vs 10.4 us (416 workgroups of 128 KB: two rounds).
 template <int D, int DT, bool CAUSAL, int NS>
 int launch_split(FwdArgs a, hipStream_t st) {
   a.units = (a.N + 31) / 32;
@@ -74,9 +78,13 @@ int pick(FwdArgs a, hipStream_t st) {
   const int64_t wg256 = (int64_t)a.B * a.H * ((a.N + 255) / 256);
   if constexpr (D == 64 || D == 128) {
     // key-split kernel while all its workgroups fit the chip at once (64 KB
-    // of LDS each at d=64: two per CU; 128 KB at d=128: one)
+    // of LDS each at d=64: two per CU; 128 KB at d=128: one); at d=64 with
+    // rows of 16 tiles or more, 8 waves per unit (128 KB: one per CU)
+    const int64_t units = (int64_t)a.B * a.H * ((a.N + 31) / 32);
+    if constexpr (D == 64)
+      if (units <= 256 && a.N >= 1024) return launch_split<D, DT, CAUSAL, 8>(a, st);
     constexpr int64_t kSplitMax = D == 64 ? 512 : 256;
-    if ((int64_t)a.B * a.H * ((a.N + 31) / 32) <= kSplitMax) return launch_split<D, DT, CAUSAL, 4>(a, st);
+    if (units <= kSplitMax) return launch_split<D, DT, CAUSAL, 4>(a, st);
   }
   if constexpr (D == 64 || D == 128) {
     if (wg256 < 256) return launch_one<D, DT, CAUSAL, 4, 1, 64, k_prefetch<D, DT, 4>()>(a, st);

@@ -59,14 +59,17 @@ def test_workload_parity(name, seed):
 
 # The dispatch runs the key-split kernel (one workgroup per 32-row unit, keys
 # split over 4 waves) while B*H*ceil(N/32) is at most 512 (d=64) or 256
-# (d=128), and the main kernel past that. Both sides of each boundary,
+# (d=128), and the main kernel past that; at d=64 it splits over 8 waves
+# while that count is at most 256 and N >= 1024. Both sides of each boundary,
 # against the oracle; long rows split over the waves with large logits
 # (rescales in the merge), and short sequences that leave waves without keys.
 @pytest.mark.parametrize("H,N,d,dtype,causal", [
     (32, 512, 64, "f16", False), (32, 513, 64, "bf16", True),
     (8, 1024, 128, "bf16", False), (8, 1025, 128, "f16", True),
     (2, 4096, 64, "bf16", False), (1, 3000, 64, "f16", True), (2, 4096, 128, "bf16", True),
-    (3, 100, 64, "bf16", True), (4, 192, 128, "f16", False)])
+    (3, 100, 64, "bf16", True), (4, 192, 128, "f16", False),
+    (8, 1024, 64, "bf16", False), (8, 1025, 64, "f16", True), (8, 1023, 64, "f16", False),
+    (1, 1024, 64, "bf16", True), (1, 8192, 64, "f16", False)])
 def test_key_split_path(H, N, d, dtype, causal):
     rows = P.sample_rows(1, H, N, 300, H + N) if H * N * N > 4 * 1024 * 1024 else None
     run_case(1, H, N, d, dtype, causal, 40 + H, None, 2.5, 1.0, rows)
@@ -313,11 +316,11 @@ def test_packed_qkv_pages_shape(d):
 # ---------------------------------------------------------------------------
 # variable-length packed batches
 # ---------------------------------------------------------------------------
-def test_varlen_small_grid():
-    # few short sequences: the key-split kernel's varlen path
-    seqlens = [400, 0, 37, 129]
-    say(f"[fa_fwd_varlen] {seqlens} d=64 bf16 causal=False/True")
-    H = 2
+@pytest.mark.parametrize("seqlens,H", [([400, 0, 37, 129], 2), ([1100, 0, 37, 2000], 1)])
+def test_varlen_small_grid(seqlens, H):
+    # few sequences: the key-split kernel's varlen path (4 waves per unit;
+    # 8 for the second set, whose longest row has 32 tiles)
+    say(f"[fa_fwd_varlen] {seqlens} H={H} d=64 bf16 causal=False/True")
     q, k, v, cu = inputs.make_varlen(seqlens, H, 64, "bf16", 82)
     qd, kd, vd = (P.decode(x, "bf16") for x in (q, k, v))
     for causal in (False, True):
