@@ -9,13 +9,46 @@
 namespace fa {
 namespace {
 
+// Blocks per head for `units` 32-row units over blocks of at most `nw`
+// waves. The fewest blocks that cover the units, unless those workgroups
+// fill the resident slots unevenly (some CUs holding one, some two): then
+// more blocks of fewer units, as long as all stay resident at once, when that
+// lowers the units the busiest CU holds, ceil(bh*n / cus) * units / n.
+// N=6400 x16 heads d=64: 400 workgroups of 8 units for 512 slots (201 us)
+// -> 512 of 6-7 units (193 us).
+int balanced_blocks(int64_t bh, int units, int nw, int cus, int per_cu) {
+  int best = (units + nw - 1) / nw;
+  if (cus <= 0 || per_cu <= 0) return best;
+  auto cost = [&](int n) { return (double)((bh * n + cus - 1) / cus) * units / n; };
+  double best_cost = cost(best);
+  for (int n = best + 1; n <= units && bh * n <= (int64_t)cus * per_cu; ++n)
+    if (cost(n) < best_cost - 1e-9) {
+      best = n;
+      best_cost = cost(n);
+    }
+  return best;
+}
+
 template <int D, int DT, bool CAUSAL, int NW, int QB, int BC, int PF>
 int launch_one(FwdArgs a, hipStream_t st) {
-  // 32-row units spread evenly over as few blocks of at most NW units as
-  // cover them (N = 400 on 4-wave blocks: 3, 3, 3 and 4 units, not 4, 4, 4, 1)
+  // 32-row units spread evenly over the blocks of a head (N = 400 on 4-wave
+  // blocks: 3, 3, 3 and 4 units, not 4, 4, 4, 1)
   static_assert(QB == 1, "one 32-row unit per wave");
   a.units = (a.N + 31) / 32;
   a.nqb = (a.units + NW - 1) / NW;
+  if (!CAUSAL && !a.cu_seqlens) {
+    // CUs and resident workgroups per CU of this kernel, queried once
+    static const int2 occ = [] {
+      int dev = 0, cus = 0, per = 0;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+          hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fa_fwd_kernel<D, DT, CAUSAL, NW, QB, BC, PF>,
+                                                       NW * 64, 0) != hipSuccess)
+        return int2{0, 0};
+      return int2{cus, per};
+    }();
+    a.nqb = balanced_blocks((int64_t)a.B * a.H, a.units, NW, occ.x, occ.y);
+  }
   const int64_t total = (int64_t)a.B * a.H * a.nqb;
   if (total > (INT64_C(1) << 30)) return FA_ERR_DIM;
   a.total = (int)total;
