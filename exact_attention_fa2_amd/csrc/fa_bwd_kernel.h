@@ -120,9 +120,11 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dkdv_kernel(const BwdArgs a) {
   static_assert(BQ * D / 8 % NT == 0, "tile must split evenly");
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SM::STAGE_HALVES];
 
+  // block order as in fa_bwd_dkdv_wide_kernel: key block major, head minor
   const int nkb = (a.N + 127) / 128;
-  const int bh = blockIdx.x / nkb, kblk = blockIdx.x - bh * nkb;
-  if (bh >= a.B * a.H) return;
+  const int BH = a.B * a.H;
+  const int kblk = blockIdx.x / BH, bh = blockIdx.x - kblk * BH;
+  if (kblk >= nkb) return;
   const int64_t off = (int64_t)bh * a.N * D;
   const uint16_t* Qg = a.q + off;
   const uint16_t* Kg = a.k + off;
@@ -329,9 +331,14 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv_wide_kernel(const B
   constexpr int VFRAG = KK * 64;                 // u32x4 per wave
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE + NW * VFRAG * 8];
 
+  // block order: key block major, head minor. Causal blocks then start
+  // longest first across all heads (a head-major order leaves the long
+  // blocks of the last heads for the end), and with B*H a multiple of the 8
+  // XCDs every block of a head lands on one XCD, sharing its Q/dO in L2.
   const int nkb = (a.N + KW - 1) / KW;
-  const int bh = blockIdx.x / nkb, kblk = blockIdx.x - bh * nkb;
-  if (bh >= a.B * a.H) return;
+  const int BH = a.B * a.H;
+  const int kblk = blockIdx.x / BH, bh = blockIdx.x - kblk * BH;
+  if (kblk >= nkb) return;
   const int64_t off = (int64_t)bh * a.N * D;
   const uint16_t* Qg = a.q + off;
   const uint16_t* Kg = a.k + off;
@@ -532,10 +539,13 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_bwd_dq_kernel(con
   constexpr int GFRAG = KK * 64;                 // u32x4 per wave
   __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE + (GL ? NW * GFRAG * 8 : 0)];
 
+  // block order: query block major (causal: longest first across all
+  // heads), head minor, as in fa_bwd_dkdv_wide_kernel
   const int nqb = (a.N + BR - 1) / BR;
-  const int bh = blockIdx.x / nqb, qblk0 = blockIdx.x - bh * nqb;
-  if (bh >= a.B * a.H) return;
-  const int qblk = CAUSAL ? nqb - 1 - qblk0 : qblk0;  // longest first
+  const int BH = a.B * a.H;
+  const int qblk0 = blockIdx.x / BH, bh = blockIdx.x - qblk0 * BH;
+  if (qblk0 >= nqb) return;
+  const int qblk = CAUSAL ? nqb - 1 - qblk0 : qblk0;
   const int64_t off = (int64_t)bh * a.N * D;
   const uint16_t* Qg = a.q + off;
   const uint16_t* Kg = a.k + off;
@@ -710,8 +720,9 @@ __global__ __launch_bounds__(NW * 64) void fa_bwd_dq_staged_kernel(const BwdArgs
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SM::STAGE];
 
   const int nqb = (a.N + BR - 1) / BR;
-  const int bh = blockIdx.x / nqb, qblk0 = blockIdx.x - bh * nqb;
-  if (bh >= a.B * a.H) return;
+  const int BH = a.B * a.H;
+  const int qblk0 = blockIdx.x / BH, bh = blockIdx.x - qblk0 * BH;
+  if (qblk0 >= nqb) return;
   const int qblk = CAUSAL ? nqb - 1 - qblk0 : qblk0;  // longest first
   const int64_t off = (int64_t)bh * a.N * D;
   const uint16_t* Qg = a.q + off;
