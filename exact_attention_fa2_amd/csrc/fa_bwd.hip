@@ -14,19 +14,19 @@ int64_t bwd_bytes(int B, int H, int N) {
   return ((int64_t)B * H * N * 4 + 255) / 256 * 256;  // D_i in fp32
 }
 
-// dK and dV in one pass with V fragments in LDS: d = 128 in 8-wave, 256-key
-// blocks (two waves per SIMD; with 8-wave dQ blocks), d = 64 in 4-wave,
-// 128-key blocks (three waves per SIMD); d = 96 in two passes. Against the
-// earlier two passes (d = 128) and fused 4-wave kernel with K and V
-// fragments in registers (d = 64, two waves per SIMD), per backward:
-// N=8192 causal bf16 d=128 3563 vs 4610 us, B4 H16 N4096 fp16 d=128 2125 vs
-// 2833 us, B4 H16 N4096 fp16 d=64 1131 vs 1203 us, N=400 x128 heads bf16
-// 52.9 vs 54.1 us. The dQ kernel with K/V by LDS-DMA (and, at d = 64, dO
-// fragments in LDS: three waves per SIMD) then took these to 3216, 1015 and
-// 49.5 us (N=8192 causal, N=4096 d=64, N=400) from 3562, 1097 and 52.2.
-// Block order key/query block major, head minor (longest first across all
-// heads when causal; a head's blocks on one XCD): N=8192 causal 3226 ->
-// 1936 us, N=400 x128 heads 51.5 -> 49.3 us, N=4096 unchanged.
+// Kernels per head dim, each at the occupancy its registers allow:
+//  * dK/dV in one pass with V fragments parked in LDS: d = 128 in 8-wave,
+//    256-key blocks (two waves per SIMD), d = 64 in 4-wave, 128-key blocks
+//    (three); d = 96 in two passes, dV then dK.
+//  * dQ with K/V tiles by LDS-DMA: 8 waves at d = 128, 4 at d = 64 (dO
+//    fragments in LDS, three waves per SIMD); the register-staged kernel at
+//    d = 96.
+// Every kernel orders its blocks key/query block major, head minor.
+// Measured per backward, same box, against the earlier two-pass dK/dV
+// (d = 128) or fused dK/dV with K/V fragments in registers (d = 64), the
+// register-staged dQ and the head-major order: N=8192 causal bf16 d=128
+// 4610 -> 1936 us, B4 H16 N4096 fp16 d=64 1203 -> 1048 us, N=400 x128 heads
+// bf16 54.1 -> 49.3 us.
 template <int D, int DT, bool CAUSAL>
 int launch(const BwdArgs& a, hipStream_t st) {
   constexpr int QNW = D == 128 ? 8 : 4;
