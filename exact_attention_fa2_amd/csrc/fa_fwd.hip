@@ -29,7 +29,7 @@ int balanced_blocks(int64_t bh, int units, int nw, int cus, int per_cu) {
   return best;
 }
 
-template <int D, int DT, bool CAUSAL, int NW, int QB, int BC, int PF>
+template <int D, int DT, bool CAUSAL, int NW, int QB, int BC, int PF, bool LS = false>
 int launch_one(FwdArgs a, hipStream_t st) {
   // 32-row units spread evenly over the blocks of a head (N = 400 on 4-wave
   // blocks: 3, 3, 3 and 4 units, not 4, 4, 4, 1)
@@ -42,7 +42,7 @@ int launch_one(FwdArgs a, hipStream_t st) {
       int dev = 0, cus = 0, per = 0;
       if (hipGetDevice(&dev) != hipSuccess ||
           hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-          hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fa_fwd_kernel<D, DT, CAUSAL, NW, QB, BC, PF>,
+          hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fa_fwd_kernel<D, DT, CAUSAL, NW, QB, BC, PF, LS>,
                                                        NW * 64, 0) != hipSuccess)
         return int2{0, 0};
       return int2{cus, per};
@@ -54,7 +54,7 @@ int launch_one(FwdArgs a, hipStream_t st) {
   a.total = (int)total;
   const int grid = (a.total + 7) / 8 * 8;  // a multiple of the 8 XCDs
   (void)hipGetLastError();
-  hipLaunchKernelGGL((fa_fwd_kernel<D, DT, CAUSAL, NW, QB, BC, PF>), dim3(grid), dim3(NW * 64), 0, st, a);
+  hipLaunchKernelGGL((fa_fwd_kernel<D, DT, CAUSAL, NW, QB, BC, PF, LS>), dim3(grid), dim3(NW * 64), 0, st, a);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -121,6 +121,13 @@ int pick(FwdArgs a, hipStream_t st) {
   }
   if constexpr (D == 64 || D == 128) {
     if (wg256 < 256) return launch_one<D, DT, CAUSAL, 4, 1, 64, k_prefetch<D, DT, 4>()>(a, st);
+  }
+  if constexpr (D == 64 && DT == DT_BF16 && !CAUSAL) {
+    // at most two 32-row units of work per SIMD (1024 SIMDs): the weight
+    // sums by MFMA (N=400 x128 heads: 14.7-15.4 vs 15.0-15.8 us; with the
+    // chip full they cost 1.5-5 %)
+    if (a.cu_seqlens == nullptr && (int64_t)a.B * a.H * ((a.N + 31) / 32) <= 2048)
+      return launch_one<D, DT, CAUSAL, 8, 1, 64, k_prefetch<D, DT, 8>(), true>(a, st);
   }
   if constexpr (D == 256)
     return launch_one<D, DT, CAUSAL, 4, 1, 32, k_prefetch<D, DT, 4>()>(a, st);

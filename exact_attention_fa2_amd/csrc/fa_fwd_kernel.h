@@ -122,12 +122,18 @@ __device__ __forceinline__ int lds_off(int row, int col) {
 // One K/V tile for one wave: Sᵀ = K Qᵀ, online-softmax update, Oᵀ += Vᵀ Pᵀ.
 // Masked tiles (wave-uniform flag) apply the ragged-tail and causal masks;
 // `first` (wave-uniform) marks the first tile of the wave's rows.
-template <int D, int DT, bool CAUSAL, int QB, int BC, int KSTR, int VSTR, int PF>
+// LS (bf16 only): the sum of the 16-bit weights is accumulated by MFMA as an
+// extra all-ones block of V, oacc[j][D/32] (every register of it holds the
+// row's full sum), instead of by dot2 instructions; the range check then uses
+// the fp32 sums. It trades 20 VALU instructions a tile for 4 MFMAs, which
+// pays only where the MFMA units have slack.
+template <int D, int DT, bool CAUSAL, int QB, int BC, int KSTR, int VSTR, int PF, bool LS = false>
 __device__ __forceinline__ void tile_step_fwd(bool first, bool masked, const uint16_t* __restrict__ sk,
                                                const uint16_t* __restrict__ sv, int key0, int Nb,
                                                int qw0, int lane, float c, const u32x4 (&qf)[QB][D / 16],
-                                               f32x16 (&oacc)[QB][D / 32], float (&m_run)[QB],
+                                               f32x16 (&oacc)[QB][D / 32 + LS], float (&m_run)[QB],
                                                float (&l_run)[2][QB]) {
+  static_assert(!LS || DT == DT_BF16, "MFMA weight sums rely on the fp32 sums of the bf16 path");
   constexpr int KK = D / 16, DB = D / 32, KB = BC / 32;
   const int l32 = lane & 31, hh = lane >> 5;
 
@@ -225,7 +231,7 @@ __device__ __forceinline__ void tile_step_fwd(bool first, bool masked, const uin
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             x[e] = pack2<DT>(p[8 * c2 + 2 * e], p[8 * c2 + 2 * e + 1]);
-            lp[e] = dot2_sum<DT>(x[e], lp[e]);
+            if constexpr (!LS) lp[e] = dot2_sum<DT>(x[e], lp[e]);
           }
           pf[j][2 * kb + c2] = x;
         }
@@ -243,7 +249,8 @@ __device__ __forceinline__ void tile_step_fwd(bool first, bool masked, const uin
     // still zero, so nothing needs rescaling)
     if (first) m_run[j] = tile_max();
     probs(m_run[j] == -INFINITY ? 0.f : m_run[j]);
-    const float pk = fmaxf(fmaxf(lp[0], lp[1]), fmaxf(lp[2], lp[3]));
+    const float pk = LS ? fmaxf(fmaxf(lf[0], lf[1]), fmaxf(lf[2], lf[3]))
+                        : fmaxf(fmaxf(lp[0], lp[1]), fmaxf(lp[2], lp[3]));
     if (wave_any(!(pk < partial_cap<DT>()))) {
       // some weight may have left the 16-bit range: raise the reference to
       // the true max, rescale what has been accumulated, redo the weights
@@ -257,13 +264,13 @@ __device__ __forceinline__ void tile_step_fwd(bool first, bool masked, const uin
       l_run[0][j] *= alpha;
       l_run[1][j] *= alpha;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB + LS; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[j][db][r] *= alpha;
       m_run[j] = m_new;
       probs(m_new == -INFINITY ? 0.f : m_new);
     }
-    l_run[0][j] += (lp[0] + lp[1]) + (lp[2] + lp[3]);
+    if constexpr (!LS) l_run[0][j] += (lp[0] + lp[1]) + (lp[2] + lp[3]);
     if constexpr (DT == DT_BF16) l_run[1][j] += (lf[0] + lf[1]) + (lf[2] + lf[3]);
   }
 
@@ -282,9 +289,16 @@ __device__ __forceinline__ void tile_step_fwd(bool first, bool masked, const uin
       for (int j = 0; j < QB; ++j) oacc[j][db] = mfma32x32x16<DT>(va, pf[j][ci], oacc[j][db]);
     }
   }
+  if constexpr (LS) {
+    const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0
+#pragma unroll
+    for (int ci = 0; ci < BC / 16; ++ci)
+#pragma unroll
+      for (int j = 0; j < QB; ++j) oacc[j][DB] = mfma32x32x16<DT>(ones, pf[j][ci], oacc[j][DB]);
+  }
 }
 
-template <int D, int DT, bool CAUSAL, int NW, int QB, int BC, int PF>
+template <int D, int DT, bool CAUSAL, int NW, int QB, int BC, int PF, bool LS = false>
 __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
   static_assert(QB == 1, "one 32-row unit per wave");
   constexpr int NT = NW * 64;
@@ -392,11 +406,11 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
   };
 
   // ---- running state ----
-  f32x16 oacc[QB][DB];
+  f32x16 oacc[QB][DB + LS];
 #pragma unroll
   for (int j = 0; j < QB; ++j)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB + LS; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[j][db][r] = 0.f;
   float m_run[QB], l_run[2][QB];
@@ -435,7 +449,7 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
       const uint16_t* sv = sk + SM::KTILE;
       // ragged last tile, or (causal) keys after some query of this wave
       const bool need_mask = (key0 + BC > Nb) || (CAUSAL && key0 + BC - 1 > qw0);
-      tile_step_fwd<D, DT, CAUSAL, QB, BC, SM::KSTR, SM::VSTR, PF>(t == 0, need_mask, sk, sv, key0, Nb, qw0,
+      tile_step_fwd<D, DT, CAUSAL, QB, BC, SM::KSTR, SM::VSTR, PF, LS>(t == 0, need_mask, sk, sv, key0, Nb, qw0,
                                                                lane, a.c, qf, oacc, m_run, l_run);
       if (t + 1 < ntiles) stash((t + 1) & 1);
     }
@@ -444,7 +458,7 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
         __syncthreads();
         if (t + 1 < ntiles) fetch(t + 1);
         const uint16_t* sk = smem + (t & 1) * SM::STAGE;
-        tile_step_fwd<D, DT, CAUSAL, QB, 32, SM::KSTR, SM::VSTR, PF>(t == 0, true, sk, sk + SM::KTILE, t * BC,
+        tile_step_fwd<D, DT, CAUSAL, QB, 32, SM::KSTR, SM::VSTR, PF, LS>(t == 0, true, sk, sk + SM::KTILE, t * BC,
                                                                  Nb, qw0, lane, a.c, qf, oacc, m_run, l_run);
         if (t + 1 < ntiles) stash((t + 1) & 1);
         ++t;
@@ -478,7 +492,7 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
   uint16_t* ob = smem + w * QW * OSTR;
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
-    const float l_tot = l_run[0][j] + xor_lane32(l_run[0][j]);
+    const float l_tot = LS ? oacc[j][DB][0] : l_run[0][j] + xor_lane32(l_run[0][j]);
     const float l_lse = DT == DT_F16 ? l_tot : l_run[1][j] + xor_lane32(l_run[1][j]);
     const float inv = 1.f / l_tot;
 #pragma unroll

@@ -179,27 +179,41 @@ def test_dominant_score_selects_row():
     P.gate_o(P.to64(o[0, 0]), ref, "f16")
 
 
+@pytest.mark.parametrize("H", [2, 64])
 @pytest.mark.parametrize("jump", [18.0, 40.0])
-def test_bf16_late_dominant_key(jump):
+def test_bf16_late_dominant_key(jump, H):
     # One late key scores `jump` (natural-log units) above every other key, so
     # its weight relative to the first tile's reference is about 2^(1.44 jump):
     # 2^26 at 18 (accepted under the 2^32 bf16 cap, no redo) and 2^58 at 40
     # (a redo and a rescale). Either way O and LSE must match the oracle.
-    say(f"[bf16] late dominant key, jump {jump}")
+    # H=2 runs the key-split kernel, H=64 the main kernel with the weight sums
+    # by MFMA (its range check on the fp32 sums); the first and last heads are
+    # compared.
+    say(f"[bf16] late dominant key, jump {jump}, H {H}")
     N, d, sc = 1000, 64, 0.125
     g = torch.Generator().manual_seed(11)
-    q = torch.zeros(1, 2, N, d)
+    q = torch.zeros(1, H, N, d)
     q[..., 0] = 1.0
-    k = torch.randn(1, 2, N, d, generator=g) * 0.05
+    k = torch.randn(1, H, N, d, generator=g) * 0.05
     k[0, :, 900] = 0.0
     k[0, :, 900, 0] = jump / sc
-    v = torch.randn(1, 2, N, d, generator=g)
+    v = torch.randn(1, H, N, d, generator=g)
     q, k, v = q.bfloat16(), k.bfloat16(), v.bfloat16()
     o, lse = _gpu(q, k, v, False, sc)
-    qd, kd, vd = (P.decode(x, "bf16") for x in (q, k, v))
-    ro, rl = oracle.attention_fwd(qd, kd, vd, sc, False)
-    P.gate_o(P.to64(o), ro, "bf16")
-    P.gate_lse(P.to64(lse), rl)
+    og, lg = P.to64(o), P.to64(lse)
+    for h in sorted({0, H - 1}):
+        qd, kd, vd = (P.decode(x[:, h:h + 1], "bf16") for x in (q, k, v))
+        ro, rl = oracle.attention_fwd(qd, kd, vd, sc, False)
+        P.gate_o(og[:, h:h + 1], ro, "bf16")
+        P.gate_lse(lg[:, h:h + 1], rl)
+
+
+@pytest.mark.parametrize("B,H,N,sigma", [(16, 8, 400, 3.0), (8, 8, 1000, 1.0), (4, 32, 500, 2.5)])
+def test_bf16_small_grid_mfma_weight_sums(B, H, N, sigma):
+    # bf16 d=64 grids of at most 2048 units of 32 rows: the main kernel forms
+    # the sums of the 16-bit weights by MFMA; large logits exercise the redo
+    rows = P.sample_rows(B, H, N, 300, N)
+    run_case(B, H, N, 64, "bf16", False, 60 + B, None, sigma, 1.0, rows)
 
 
 def test_deterministic():
