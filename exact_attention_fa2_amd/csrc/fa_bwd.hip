@@ -37,20 +37,21 @@ int launch(const BwdArgs& a, hipStream_t st) {
   if (gdot > (INT64_C(1) << 31) - 1 || gk > (INT64_C(1) << 31) - 1 || gq > (INT64_C(1) << 31) - 1)
     return FA_ERR_DIM;
   (void)hipGetLastError();
-  hipLaunchKernelGGL((fa_bwd_dot_kernel<D, DT>), dim3((unsigned)gdot), dim3(256), 0, st, a);
-  if constexpr (D == 128) {
-    const int64_t gw = (int64_t)a.B * a.H * ((a.N + 255) / 256);
-    hipLaunchKernelGGL((fa_bwd_dkdv_wide_kernel<D, DT, CAUSAL, 8, 1>), dim3((unsigned)gw), dim3(512), 0, st, a);
-  } else if constexpr (D == 96) {
+  if constexpr (D == 96) {
+    hipLaunchKernelGGL((fa_bwd_dot_kernel<D, DT>), dim3((unsigned)gdot), dim3(256), 0, st, a);
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, DT, CAUSAL, BWD_DV>), dim3((unsigned)gk), dim3(256), 0, st, a);
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, DT, CAUSAL, BWD_DK>), dim3((unsigned)gk), dim3(256), 0, st, a);
-  } else {
-    hipLaunchKernelGGL((fa_bwd_dkdv_wide_kernel<D, DT, CAUSAL, 4, 3>), dim3((unsigned)gk), dim3(256), 0, st, a);
-  }
-  if constexpr (D == 96)
     hipLaunchKernelGGL((fa_bwd_dq_staged_kernel<D, DT, CAUSAL, QNW>), dim3((unsigned)gq), dim3(QNW * 64), 0, st, a);
-  else
+  } else {
+    // dQ first: it also forms and stores D_i, which dK/dV reads
     hipLaunchKernelGGL((fa_bwd_dq_kernel<D, DT, CAUSAL, QNW>), dim3((unsigned)gq), dim3(QNW * 64), 0, st, a);
+    if constexpr (D == 128) {
+      const int64_t gw = (int64_t)a.B * a.H * ((a.N + 255) / 256);
+      hipLaunchKernelGGL((fa_bwd_dkdv_wide_kernel<D, DT, CAUSAL, 8, 1>), dim3((unsigned)gw), dim3(512), 0, st, a);
+    } else {
+      hipLaunchKernelGGL((fa_bwd_dkdv_wide_kernel<D, DT, CAUSAL, 4, 3>), dim3((unsigned)gk), dim3(256), 0, st, a);
+    }
+  }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -7,7 +7,8 @@
 //   dK = scale · dSᵀ Q,  dQ = scale · dS K.
 //
 // MI355X layout (our design): three kernels and no atomics.
-//  * fa_bwd_dot_kernel: D_i in fp32.
+//  * fa_bwd_dot_kernel (d = 96): D_i in fp32. At d = 64 and 128 the dQ
+//    kernel forms D_i for its own rows and stores it; it runs first.
 //  * fa_bwd_dkdv_wide_kernel (d = 64, 128): one workgroup per block of keys,
 //    each wave owning 32 keys; 64-query tiles of Q, dO, LSE and D stream
 //    through LDS. S and dP are computed with the key in the lane (S = Q Kᵀ),
@@ -558,22 +559,34 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_bwd_dq_kernel(con
   const int qw0 = qblk * BR + w * 32;
   const int qrow = qw0 + l32;
 
+  // Q and dO fragments of this lane's row (its half of the d columns), and
+  // D_i = <dO_i, O_i> from the same half of O plus the partner lane's half.
+  // D_i is also stored for the dK/dV kernel, which runs after this one.
   u32x4 qf[KK], gf[GL ? 1 : KK];
   u32x4* gl = (u32x4*)(smem + 4 * TILE) + w * GFRAG;
+  const uint16_t* Og = a.o + off;
+  float dpart = 0.f;
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     const int rr = min(qrow, N - 1);
     const u32x4 x = *(const u32x4*)(Qg + (int64_t)rr * D + 16 * kk + 8 * hh);
     const u32x4 y = *(const u32x4*)(Gg + (int64_t)rr * D + 16 * kk + 8 * hh);
+    const u32x4 ov = *(const u32x4*)(Og + (int64_t)rr * D + 16 * kk + 8 * hh);
     qf[kk] = (qrow < N ? x : u32x4{0u, 0u, 0u, 0u}) ^ a.qsign;
     const u32x4 g = qrow < N ? y : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dpart += to_f32<DT>((uint16_t)(g[e] & 0xFFFF)) * to_f32<DT>((uint16_t)(ov[e] & 0xFFFF));
+      dpart += to_f32<DT>((uint16_t)(g[e] >> 16)) * to_f32<DT>((uint16_t)(ov[e] >> 16));
+    }
     if constexpr (GL)
       gl[kk * 64 + lane] = g;
     else
       gf[kk] = g;
   }
   const float lq = qrow < N ? a.lse[(int64_t)bh * N + qrow] * kLog2e : INFINITY;
-  const float dq_row = qrow < N ? a.dvec[(int64_t)bh * N + qrow] : 0.f;
+  const float dq_row = dpart + xor_lane32(dpart);
+  if (hh == 0 && qrow < N) a.dvec[(int64_t)bh * N + qrow] = dq_row;
 
   f32x16 dqacc[DB];
 #pragma unroll
