@@ -131,9 +131,10 @@ int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *l
  *                     16-byte aligned, owned by the caller; contents on entry
  *                     are ignored. It holds the fp32 row terms D_i = <dO_i, O_i>.
  * Head dims 64, 96 and 128 (d = 256 returns FA_ERR_UNSUPPORTED). The kernels
- * enqueued on `stream` are D_i, then dK/dV (parallel over key blocks; at
- * d = 96 two passes, dV then dK), then dQ (parallel over query blocks).
- * There are no atomics, so results are deterministic.
+ * enqueued on `stream`: at d = 64 and 128, dQ (parallel over query blocks;
+ * it also forms D_i) then dK/dV (parallel over key blocks); at d = 96, D_i,
+ * then dK/dV as two passes (dV, then dK), then dQ. There are no atomics, so
+ * results are deterministic.
  */
 int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *do_,
            const float *lse, void *dq, void *dk, void *dv, void *workspace,
