@@ -313,19 +313,32 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SM::STAGE];
 
   // ---- workgroup -> (batch, head, query block), XCD-aware ----
-  // Workgroups are dealt round-robin over the 8 XCDs. With equal-length
-  // sequences each XCD takes a contiguous run of whole heads, whose blocks
-  // then share K/V in that XCD's L2. Packed sequences of different lengths
-  // keep the plain order instead: a contiguous run would hand the long
-  // sequences to a few XCDs, while the plain order spreads every sequence's
-  // blocks over all eight (re-reads of K/V across XCDs hit the shared
-  // Infinity Cache).
-  const int per = gridDim.x >> 3;
+  // Workgroups are dealt round-robin over the 8 XCDs and dispatched in
+  // order. Equal-length sequences:
+  //  * non-causal: each XCD takes a contiguous run of whole heads, whose
+  //    blocks then share K/V in that XCD's L2;
+  //  * causal: block rank major, head minor, so that the longest blocks of
+  //    every head start first (a head-major order leaves long blocks of the
+  //    last heads for the end), and with B*H a multiple of 8 every block of
+  //    a head still lands on one XCD.
+  // Packed sequences of different lengths keep the plain order: a contiguous
+  // run would hand the long sequences to a few XCDs, while the plain order
+  // spreads every sequence's blocks over all eight (re-reads of K/V across
+  // XCDs hit the shared Infinity Cache).
   const int bid = blockIdx.x;
-  const int lid = a.cu_seqlens ? bid : (bid & 7) * per + (bid >> 3);
-  if (lid >= a.total) return;
-  const int bh = lid / a.nqb;
-  const int qi = lid - bh * a.nqb;
+  int bh, qi;
+  if (CAUSAL && !a.cu_seqlens) {
+    const int nbh = a.B * a.H;
+    qi = bid / nbh;
+    bh = bid - qi * nbh;
+    if (qi >= a.nqb) return;
+  } else {
+    const int per = gridDim.x >> 3;
+    const int lid = a.cu_seqlens ? bid : (bid & 7) * per + (bid >> 3);
+    if (lid >= a.total) return;
+    bh = lid / a.nqb;
+    qi = lid - bh * a.nqb;
+  }
   const int qblk = CAUSAL ? (a.nqb - 1 - qi) : qi;
   const int b = bh / a.H, h = bh - b * a.H;
 
