@@ -6,7 +6,9 @@
 //   dV = Pᵀ dO,  dS = P ∘ (dP - D),  D_i = <dO_i, O_i>,
 //   dK = scale · dSᵀ Q,  dQ = scale · dS K.
 //
-// MI355X layout (our design): three kernels and no atomics.
+// MI355X layout (our design), no atomics: two kernels at d = 64 and 128 (dQ,
+// which also forms D_i, then dK/dV), four at d = 96. Blocks are ordered key
+// or query block major, head minor.
 //  * fa_bwd_dot_kernel (d = 96): D_i in fp32. At d = 64 and 128 the dQ
 //    kernel forms D_i for its own rows and stores it; it runs first.
 //  * fa_bwd_dkdv_wide_kernel (d = 64, 128): one workgroup per block of keys,

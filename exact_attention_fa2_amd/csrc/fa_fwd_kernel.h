@@ -27,7 +27,8 @@
 //    standing m and only their partial sums are checked; a tile whose
 //    partial sums reach partial_cap (so some weight could leave the 16-bit
 //    range) is redone with the true max and a rescale of the output
-//    accumulator. O = acc / l and LSE = (m + log2 l) ln 2 are exact for any
+//    accumulator. In the bf16 kernel for small grids the sum of the 16-bit
+//    weights comes from the MFMA units (an all-ones block of V). O = acc / l and LSE = (m + log2 l) ln 2 are exact for any
 //    reference m, so only the range of p matters, not which m is used.
 //  * K/V for tile t+1 are fetched into registers (buffer loads whose
 //    descriptor covers only the tile's valid rows: rows past the end read
@@ -36,7 +37,7 @@
 //  * Workgroup ids are remapped so that each XCD (workgroups are dealt
 //    round-robin over the 8 XCDs) walks whole heads, sharing K/V in its L2
 //    (packed batches of unequal sequences keep the plain order); causal
-//    blocks run longest first.
+//    blocks run by rank across all heads, longest first.
 //  * A head's 32-row units are spread evenly over its blocks, one unit per
 //    wave; waves without a unit only help with the K/V loads.
 #pragma once
