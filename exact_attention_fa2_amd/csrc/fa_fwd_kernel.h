@@ -321,7 +321,10 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
   //  * causal: block rank major, head minor, so that the longest blocks of
   //    every head start first (a head-major order leaves long blocks of the
   //    last heads for the end), and with B*H a multiple of 8 every block of
-  //    a head still lands on one XCD.
+  //    a head still lands on one XCD. With long rows (32 or more blocks a
+  //    head) and B*H a multiple of 16, each XCD takes its heads in pairs,
+  //    rank major within a pair: as fast, with two heads' K/V in flight per
+  //    XCD instead of all of them (N=8192 x32 heads: 0.63x the fetched bytes).
   // Packed sequences of different lengths keep the plain order: a contiguous
   // run would hand the long sequences to a few XCDs, while the plain order
   // spreads every sequence's blocks over all eight (re-reads of K/V across
@@ -330,9 +333,17 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
   int bh, qi;
   if (CAUSAL && !a.cu_seqlens) {
     const int nbh = a.B * a.H;
-    qi = bid / nbh;
-    bh = bid - qi * nbh;
-    if (qi >= a.nqb) return;
+    if ((nbh & 15) == 0 && a.nqb >= 32) {
+      const int x = bid & 7, j = bid >> 3;  // XCD, position in its order
+      const int grp = j / (2 * a.nqb), r = j - grp * 2 * a.nqb;
+      qi = r >> 1;
+      bh = x + 8 * (2 * grp + (r & 1));
+      if (bh >= nbh) return;
+    } else {
+      qi = bid / nbh;
+      bh = bid - qi * nbh;
+      if (qi >= a.nqb) return;
+    }
   } else {
     const int per = gridDim.x >> 3;
     const int lid = a.cu_seqlens ? bid : (bid & 7) * per + (bid >> 3);

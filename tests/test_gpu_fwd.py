@@ -75,6 +75,16 @@ def test_key_split_path(H, N, d, dtype, causal):
     run_case(1, H, N, d, dtype, causal, 40 + H, None, 2.5, 1.0, rows)
 
 
+@pytest.mark.parametrize("B,H,N,d,dtype", [(2, 8, 8192, 64, "f16"), (1, 16, 8200, 128, "bf16"),
+                                           (1, 12, 4096, 128, "bf16"), (3, 8, 2000, 64, "bf16")])
+def test_causal_block_orders(B, H, N, d, dtype):
+    # causal launches order blocks by rank across heads; B*H a multiple of 16
+    # with 32+ blocks a head takes the heads in pairs per XCD (the first two
+    # shapes), other head counts the plain rank order (the last two)
+    rows = P.sample_rows(B, H, N, 300, B * H + N)
+    run_case(B, H, N, d, dtype, True, 70 + H, None, 2.0, 1.0, rows)
+
+
 def test_long_causal_variance3_reading():
     # the other reading of the large-logit workload: variance 3 (sigma = sqrt 3)
     w = inputs.WORKLOADS["n8192_causal"]
