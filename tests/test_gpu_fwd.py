@@ -69,7 +69,8 @@ def test_workload_parity(name, seed):
     (2, 4096, 64, "bf16", False), (1, 3000, 64, "f16", True), (2, 4096, 128, "bf16", True),
     (3, 100, 64, "bf16", True), (4, 192, 128, "f16", False),
     (8, 1024, 64, "bf16", False), (8, 1025, 64, "f16", True), (8, 1023, 64, "f16", False),
-    (1, 1024, 64, "bf16", True), (1, 8192, 64, "f16", False)])
+    (1, 1024, 64, "bf16", True), (1, 8192, 64, "f16", False),
+    (4, 400, 64, "f16", False), (2, 1000, 64, "bf16", True), (8, 1000, 64, "f16", False)])
 def test_key_split_path(H, N, d, dtype, causal):
     rows = P.sample_rows(1, H, N, 300, H + N) if H * N * N > 4 * 1024 * 1024 else None
     run_case(1, H, N, d, dtype, causal, 40 + H, None, 2.5, 1.0, rows)
