@@ -39,8 +39,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-# the sources the forward kernel is built from (its code and its dispatch)
-FWD_SOURCES = ("fa_device.h", "fa_fwd_kernel.h", "fa_fwd.hip", "fa_fwd_split.h")
+# the files the forward kernels are built from (code, dispatch, build options)
+FWD_SOURCES = ("csrc/fa_device.h", "csrc/fa_fwd_kernel.h", "csrc/fa_fwd.hip", "csrc/fa_fwd_split.h",
+               "csrc/fa_fwd_launch.h", "csrc/fa_fwd_small.hip", "build.py")
 
 
 def kernel_source_hash() -> str:
@@ -48,7 +49,7 @@ def kernel_source_hash() -> str:
     while it matches."""
     h = hashlib.sha256()
     for name in FWD_SOURCES:
-        with open(os.path.join(ROOT, "exact_attention_fa2_amd", "csrc", name), "rb") as f:
+        with open(os.path.join(ROOT, "exact_attention_fa2_amd", name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 

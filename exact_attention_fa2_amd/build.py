@@ -33,9 +33,16 @@ FLAGS = [
 ]
 
 
+# per-file options: the small-grid forward kernels schedule for instruction-
+# level parallelism (measured faster there, slower on the large grids)
+EXTRA = {
+    "fa_fwd_small.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
