@@ -23,3 +23,16 @@ def test_launcher_world_size_is_refused():
     r = _run([], {"WORLD_SIZE": "8"})
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_forward_source_hash_files_exist():
+    # stored HBM counters are keyed by a hash of these files; each must exist
+    sys.path.insert(0, ROOT)
+    import bench
+    from exact_attention_fa2_amd import build
+    for name in bench.FWD_SOURCES:
+        assert os.path.exists(os.path.join(ROOT, "exact_attention_fa2_amd", name)), name
+    assert len(bench.kernel_source_hash()) == 16
+    # per-file compiler options name existing sources
+    for name in build.EXTRA:
+        assert os.path.exists(os.path.join(build.CSRC, name)), name
