@@ -22,7 +22,7 @@ int64_t bwd_bytes(int B, int H, int N) {
 //    fragments in LDS, three waves per SIMD); the register-staged kernel at
 //    d = 96.
 // Every kernel orders its blocks key/query block major, head minor.
-// Measured per backward, same box, against the earlier two-pass dK/dV
+// Measured per backward, same GPU, against the earlier two-pass dK/dV
 // (d = 128) or fused dK/dV with K/V fragments in registers (d = 64), the
 // register-staged dQ and the head-major order: N=8192 causal bf16 d=128
 // 4610 -> 1936 us, B4 H16 N4096 fp16 d=64 1203 -> 1048 us, N=400 x128 heads

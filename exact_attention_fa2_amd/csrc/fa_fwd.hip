@@ -8,6 +8,24 @@
 namespace fa {
 namespace {
 
+// Variant choice, from same-run measurements on MI355X (kernel time per
+// launch): 8 waves (256 query rows) per workgroup whenever the grid fills the
+// chip (N=6400 d64: 206 us, N=4096 d64: 293 us, N=400 x128 heads: 15.5 us,
+// N=8192 causal d128: 632 us); when B*H*ceil(N/256) is below the 256 CUs,
+// 4 waves (128 rows) per workgroup for more parallelism (N=400 x4 heads:
+// 9.8 us vs 11.8 us). d=96 uses 4 waves (its registers allow no more); d=256
+// uses 4 waves and 32-key tiles.
+//
+// The key-split kernel (4 waves per 32-row unit, one K/V buffer per wave)
+// runs while its B*H*ceil(N/32) workgroups all fit the chip at once: at most
+// 512 at d=64 (64 KB of LDS each, two per CU), 256 at d=128 (128 KB, one per
+// CU). Against the 4-wave kernel, same GPU: d=64 N=400 x4 heads 8.1 vs
+// 9.8 us, N=4096 x2 heads 30.4 vs 56.6 us, N=512 x32 heads 11.0 vs 11.9 us;
+// d=128 N=2048 x4 heads 33.2 vs 46.4 us, N=4096 x2 heads causal 52.2 vs
+// 85.1 us, N=400 x8 heads 12.8 vs 14.2 us. Past that size it loses (d=64
+// N=512 x64 heads 19.8 vs 13.5 us; d=128 N=1024 x16 heads 38.0 vs 27.4 us):
+// each K/V tile is reused 4x less, and a second round of workgroups follows
+// the first.
 template <int D, int DT, bool CAUSAL>
 int pick(FwdArgs a, hipStream_t st) {
   const int64_t wg256 = (int64_t)a.B * a.H * ((a.N + 255) / 256);

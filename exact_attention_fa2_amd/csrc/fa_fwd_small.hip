@@ -1,6 +1,6 @@
 // The small-grid forward kernels: the key-split kernel and the bf16 d = 64
 // kernel with MFMA weight sums. The build compiles this file with the
-// scheduler's max-ILP strategy. Against the default strategy, same box, four
+// scheduler's max-ILP strategy. Against the default strategy, same GPU, four
 // alternations each: N=400 x128 heads bf16 14.3-14.7 vs 15.3-15.6 us, N=400 x4
 // heads fp16 7.93-7.95 vs 8.04-8.09 us. The large-grid kernels in fa_fwd.hip
 // keep the default, which is faster there (N=8192 causal d=128: 562 vs
