@@ -1,15 +1,21 @@
 #!/usr/bin/env python3
 """Benchmark of the attention forward hot path on one MI355X.
 
-One step = one ``fa_fwd`` launch over one batch of synthetic input of the
-chosen workload (default: 16x8 heads of a 20x20 map, N=400, d=64, bf16).
-Inputs are resident in HBM before timing; R rotating input sets (>= 512 MB
-in total) keep the 256 MB Infinity Cache from serving them between steps.
-The K timed launches are captured once in a HIP graph and replayed, so the
-host's launch overhead cannot starve the GPU; HIP events recorded on the
-launch stream give the average kernel duration used for the roofline. After
-the W warmup steps, untimed replays run for --settle seconds: kernel times
-keep falling for tens of milliseconds after a burst starts (clocks, address
+One step = one ``fa_fwd`` launch over one batch of synthetic input. With no
+flags the headline is the largest single-GPU workload (a causal N=8192,
+32-head, d=128 bf16 long-sequence head group), timed for exactly --steps
+steps, and the same JSON line carries a record for each of the five
+workloads (N=400 x4 heads fp16, N=400 x128 heads bf16, N=6400, N=4096 and
+N=8192 causal), each timed on its own after the headline, so that one run
+measures the metric over its whole N=400..8192 range.
+
+Inputs are resident in HBM before timing; R rotating input sets (>= 512 MB in
+total) keep the 256 MB Infinity Cache from serving them between steps. The
+timed launches are captured once in a HIP graph and replayed, so the host's
+launch overhead cannot starve the GPU; HIP events recorded on the launch
+stream give the average kernel duration used for the roofline. After the W
+warmup steps, untimed replays run for --settle seconds: kernel times keep
+falling for tens of milliseconds after a burst starts (clocks, address
 translation), and the timed steps should see the steady state.
 
 Prints ONE JSON line on stdout (details go to stderr).
@@ -30,9 +36,14 @@ sys.path.insert(0, ROOT)
 from exact_attention_fa2_amd import accounting as acc  # noqa: E402
 from exact_attention_fa2_amd import inputs  # noqa: E402
 
-DEFAULT_WORKLOAD = "n400_batched"
+DEFAULT_WORKLOAD = "n8192_causal"
+# the five workloads of the metric, smallest first
+CONFIG_ORDER = ("n400_small", "n400_batched", "n6400", "n4096", "n8192_causal")
 METRIC = "attn fwd TFLOP/s (4·B·H·N²·d) and % of MFMA peak / HBM GB/s, N=400..8192"
 ROTATE_BYTES = 512 << 20
+# per-workload records: replays of the K-step graph are repeated until the
+# timed region lasts at least this long
+PER_CONFIG_MIN_S = 0.03
 
 
 def log(*a):
@@ -67,38 +78,108 @@ def stored_traffic(workload: str):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(w: inputs.Workload, budget_s: float):
-    """Times the fp64 oracle on the host on a bounded sample of the workload."""
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on the host, on a bounded sample
+# ---------------------------------------------------------------------------
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_rate(w: inputs.Workload, budget_s: float, chunk: int = 512):
+    """Algorithmic GFLOP/s of the oracle on chunks of `chunk` query rows of the
+    workload's (batch, head) slices (seed-0 inputs), until `budget_s` has
+    passed (at least one chunk). Chunk j takes head j mod B*H and row block
+    j mod ceil(N/chunk), so every run of consecutive chunks covers all row
+    ranges of a causal problem in turn. Returns (GFLOP/s, chunks, seconds)."""
     import numpy as np
-    import threadpoolctl
 
     import oracle
 
     q, k, v = inputs.make_workload(w, seed=0)
-    qd, kd, vd = (oracle.decode(inputs.bits(x), w.dtype) for x in (q, k, v))
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
-    # sample: whole (batch, head) slices taken in order (wrapping around), until
-    # the time budget is spent; at least one slice
-    done, t0 = 0, time.perf_counter()
+    nblk = (w.N + chunk - 1) // chunk
+    cache = {}
+
+    def head(b, h):
+        if (b, h) not in cache:
+            cache.clear()
+            cache[(b, h)] = tuple(oracle.decode(inputs.bits(x[b:b + 1, h:h + 1]), w.dtype) for x in (q, k, v))
+        return cache[(b, h)]
+
+    flops, done, spent = 0, 0, 0.0
     while True:
         b, h = heads[done % len(heads)]
-        oracle.attention_fwd(qd[b:b + 1, h:h + 1], kd[b:b + 1, h:h + 1], vd[b:b + 1, h:h + 1], w.scale, w.causal)
+        r0 = (done % nblk) * chunk
+        r1 = min(w.N, r0 + chunk)
+        qd, kd, vd = head(b, h)  # decoding is not timed
+        rows = np.stack([np.zeros(r1 - r0, np.int64), np.zeros(r1 - r0, np.int64),
+                         np.arange(r0, r1, dtype=np.int64)], axis=1)
+        t0 = time.perf_counter()
+        oracle.attention_fwd_rows(qd, kd, vd, w.scale, w.causal, rows)
+        spent += time.perf_counter() - t0
+        # algorithmic FLOP of these rows: 4*d per scored (query, key) pair
+        pairs = ((r0 + 1 + r1) * (r1 - r0) // 2) if w.causal else (r1 - r0) * w.N
+        flops += 4 * w.d * pairs
         done += 1
-        if time.perf_counter() - t0 > budget_s:
+        if spent > budget_s:
             break
-    dt = time.perf_counter() - t0
-    flops = acc.metric_flops(1, done, w.N, w.d)
-    threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
-    return {
-        "value": flops / dt / 1e12,
+    return flops / spent / 1e9, done, spent
+
+
+def cpu_baseline(head_w: inputs.Workload, budget_s: float, per_config: bool):
+    """The oracle timed on this host: all the threads this process may use
+    (its CPU share) and one thread, on the headline workload; optionally a
+    shorter all-threads sample of every other workload."""
+    import threadpoolctl
+
+    host_cpus = os.cpu_count() or 1
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except AttributeError:
+        allowed = host_cpus
+    env_threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    threads = min(allowed, env_threads) if env_threads > 0 else allowed
+    with threadpoolctl.threadpool_limits(limits=threads):
+        g_all, n_all, s_all = _oracle_rate(head_w, budget_s * 0.4)
+        others = {}
+        if per_config:
+            for name in CONFIG_ORDER:
+                if name != head_w.name:
+                    g, n, s = _oracle_rate(inputs.WORKLOADS[name], budget_s * 0.1)
+                    others[name] = {"gflops": round(g, 2), "chunks": n, "seconds": round(s, 2)}
+    with threadpoolctl.threadpool_limits(limits=1):
+        g_one, n_one, s_one = _oracle_rate(head_w, budget_s * 0.2)
+    out = {
+        "value": g_all / 1e3,
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": threads,
         "kind": "oracle",
-        "sample": f"{done} (batch, head) slices (the workload has {len(heads)}) of {w.name} "
-                  f"(N={w.N}, d={w.d}), fp64 numpy/OpenBLAS, {dt:.1f} s",
+        "sample": (f"{head_w.name}: {n_all} chunks of 512 query rows (of {head_w.B * head_w.H} heads x "
+                   f"{math.ceil(head_w.N / 512)} row blocks), fp64 numpy/OpenBLAS, {s_all:.1f} s on {threads} "
+                   f"threads; algorithmic FLOP (causal: kept pairs only)"),
+        "gflops_all_threads": round(g_all, 2),
+        "gflops_1_thread": round(g_one, 2),
+        "sample_1_thread": f"{n_one} chunks, {s_one:.1f} s",
+        "host_cpu_count": host_cpus,
+        "affinity_cpus": allowed,
+        "omp_num_threads": env_threads or None,
+        "cpu_model": cpu_model(),
     }
+    if others:
+        out["per_config_gflops_all_threads"] = others
+    return out
 
 
+# ---------------------------------------------------------------------------
+# GPU timing
+# ---------------------------------------------------------------------------
 def copy_bandwidth(torch, dev, stream, mib: int = 256, reps: int = 20) -> float:
     """GB/s of a plain device-to-device copy (bytes read + bytes written), timed
     with HIP events on `stream`: the bandwidth an HBM-bound kernel can reach
@@ -118,6 +199,137 @@ def copy_bandwidth(torch, dev, stream, mib: int = 256, reps: int = 20) -> float:
     gbs = 2 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
     return gbs
+
+
+def run_timed(torch, stream, launch, K: int, warmup: int, settle: float, eager: bool, check=None,
+              min_seconds: float = 0.0):
+    """Warmup, graph capture of K launches, settle, then the timed region.
+
+    The timed region replays the K-launch graph once, or (min_seconds > 0)
+    `reps` times, with reps chosen from an untimed replay so that it lasts at
+    least min_seconds. Returns (wall seconds per step, kernel seconds per step
+    from events on `stream`, steps timed, graph used)."""
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            launch(i)
+    torch.cuda.synchronize()
+    before = check() if (check and warmup > 0) else None
+    graph = None
+    if not eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(K):
+                launch(i)
+        torch.cuda.synchronize()
+        graph.replay()  # untimed replay: the graph must reproduce the eager output
+        torch.cuda.synchronize()
+        if before is not None and not torch.equal(check(), before):
+            raise RuntimeError("graph replay disagrees with the eager launch")
+
+    def one_pass():
+        if graph is not None:
+            graph.replay()
+        else:
+            for i in range(K):
+                launch(i)
+
+    t_set = time.perf_counter()
+    with torch.cuda.stream(stream):
+        while time.perf_counter() - t_set < settle:
+            one_pass()
+            torch.cuda.synchronize()
+    reps = 1
+    if min_seconds > 0:
+        t0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            one_pass()
+        torch.cuda.synchronize()
+        per_pass = max(time.perf_counter() - t0, 1e-6)
+        reps = max(1, min(500, math.ceil(min_seconds / per_pass)))
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        for _ in range(reps):
+            one_pass()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    steps = K * reps
+    return wall / steps, ev0.elapsed_time(ev1) * 1e-3 / steps, steps, graph is not None
+
+
+def make_sets(torch, dev, w: inputs.Workload, R: int, layout: str = "bhnd"):
+    """R input sets of the workload on the GPU: set 0 is the seeded CPU recipe
+    (the one the oracle and the parity tests use); the rotation sets draw the
+    same distributions from a seeded device generator."""
+    g = torch.Generator(device=dev)
+    sets = []
+    for r in range(R):
+        if r == 0:
+            q, k, v = (t.to(dev) for t in inputs.make_workload(w, seed=0))
+        else:
+            g.manual_seed(r)
+            dt = inputs.torch_dtype(w.dtype)
+            shape = (w.B, w.H, w.N, w.d)
+            q, k, v = ((torch.randn(shape, generator=g, device=dev) * s).to(dt)
+                       for s in (w.sigma_qk, w.sigma_qk, w.sigma_v))
+        if layout == "bnhd":
+            q, k, v = (t.transpose(1, 2).contiguous() for t in (q, k, v))
+        elif layout == "qkvpacked":
+            qkv = torch.stack([t.transpose(1, 2) for t in (q, k, v)], dim=2).contiguous()
+            q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+        o = torch.empty_like(q) if layout == "bhnd" else torch.empty(
+            (w.B, w.N, w.H, w.d), dtype=q.dtype, device=dev)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        sets.append((q, k, v, o, lse))
+    return sets
+
+
+def roofline(aflops: int, abytes: int, kern_s: float) -> dict:
+    """Bound, achieved rate and fraction of peak of one launch (algorithmic
+    FLOP or bytes over the kernel's average duration)."""
+    ridge = acc.MFMA_PEAK_TFLOPS_16BIT * 1e12 / (acc.HBM_PEAK_GBS * 1e9)
+    if aflops / abytes < ridge:
+        achieved, peak, unit, bound = abytes / kern_s / 1e9, acc.HBM_PEAK_GBS, "GB/s", "hbm"
+    else:
+        achieved, peak, unit, bound = aflops / kern_s / 1e12, acc.MFMA_PEAK_TFLOPS_16BIT, "TFLOP/s", "mfma"
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4)}
+
+
+def bench_fwd_workload(torch, fa, dev, stream, w: inputs.Workload, K: int, warmup: int, settle: float,
+                       eager: bool, warm_cache: bool, min_seconds: float, layout: str = "bhnd") -> dict:
+    """Times fa_fwd (or fa_fwd_strided for the other layouts) on one workload."""
+    abytes = acc.alg_bytes(w.B, w.H, w.N, w.d, 2)
+    aflops = acc.alg_flops(w.B, w.H, w.N, w.d, w.causal)
+    R = 1 if warm_cache else max(1, math.ceil(ROTATE_BYTES / abytes))
+    sets = make_sets(torch, dev, w, R, layout)
+    torch.cuda.synchronize()
+
+    def launch(i):
+        q, k, v, o, lse = sets[i % R]
+        if layout != "bhnd":
+            st = fa._strides_bnhd
+            fa.fa_fwd_strided(q, k, v, o, lse, w.B, w.H, w.N, w.d, w.scale, w.causal,
+                              st(q), st(k), st(v), st(o))
+        else:
+            fa.fa_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.d, w.scale, w.causal)
+
+    wall, kern, steps, graph = run_timed(torch, stream, launch, K, warmup, settle, eager,
+                                         check=lambda: sets[0][3].clone(), min_seconds=min_seconds)
+    del sets
+    rec = {"kernel_us": round(kern * 1e6, 3), "wall_us_per_step": round(wall * 1e6, 3), "steps": steps,
+           "input_sets": R, "alg_flop": aflops, "alg_bytes": abytes,
+           "tflops_alg": round(aflops / kern / 1e12, 2), "gbs_alg": round(abytes / kern / 1e9, 1)}
+    rec["roofline"] = roofline(aflops, abytes, kern)
+    rec["roofline"]["traffic"] = stored_traffic(w.name) if layout == "bhnd" else None
+    rec["_wall"], rec["_kern"], rec["_graph"] = wall, kern, graph
+    log(f"{w.name} ({w.describe()}): kernel {kern*1e6:.2f} us (events, {steps} steps, {R} input sets), "
+        f"wall {wall*1e6:.2f} us/step; {aflops/kern/1e12:.1f} TFLOP/s alg "
+        f"({rec['roofline']['frac']:.3f} of {rec['roofline']['bound']} peak), {abytes/kern/1e9:.0f} GB/s alg")
+    return rec
 
 
 def bench_varlen(args, torch, fa, dev) -> int:
@@ -140,34 +352,12 @@ def bench_varlen(args, torch, fa, dev) -> int:
         q, k, v, cu, o, lse = sets[i % R]
         fa.fa_fwd_varlen(q, k, v, o, lse, cu, len(seqlens), T, max(seqlens), H, d, scale, vm["causal"])
 
-    with torch.cuda.stream(stream):
-        for i in range(args.warmup):
-            launch(i)
-    torch.cuda.synchronize()
-    K = args.steps
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
-        for i in range(K):
-            launch(i)
-    torch.cuda.synchronize()
-    t_set = time.perf_counter()
-    while time.perf_counter() - t_set < args.settle:
-        graph.replay()
-        torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        ev0.record(stream)
-        graph.replay()
-        ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_s = ev0.elapsed_time(ev1) * 1e-3 / K
+    wall, kern_s, K, _ = run_timed(torch, stream, launch, args.steps, args.warmup, args.settle, args.eager)
     log(f"varlen_mix: {len(seqlens)} sequences {sorted(set(seqlens))}, T={T}, H={H}, d={d}: kernel avg "
         f"{kern_s*1e6:.2f} us; {aflops/kern_s/1e12:.1f} TFLOP/s alg")
     print(json.dumps({
-        "metric": "attn fwd TFLOP/s, packed variable-length batch", "value": round(aflops / (wall / K) / 1e12, 3),
-        "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / K, 5),
+        "metric": "attn fwd TFLOP/s, packed variable-length batch", "value": round(aflops / wall / 1e12, 3),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": vm["dtype"], "data": "synthetic",
         "config": {"workload": "varlen_mix", "seqlens": seqlens, "H": H, "d": d, "input_sets": R},
         "roofline": {"bound": "mfma", "achieved": round(aflops / kern_s / 1e12, 2),
@@ -177,16 +367,72 @@ def bench_varlen(args, torch, fa, dev) -> int:
     return 0
 
 
+def bench_other_impl(args, torch, fa, dev, w: inputs.Workload) -> int:
+    """The FA1 loop-order ablation or the backward on one workload."""
+    elem = 2
+    aflops = acc.alg_flops(w.B, w.H, w.N, w.d, w.causal)
+    mflops = acc.metric_flops(w.B, w.H, w.N, w.d)
+    abytes = acc.alg_bytes(w.B, w.H, w.N, w.d, elem)
+    metric = METRIC
+    if args.impl == "bwd":
+        # backward: five N x N x d products (S, dP, dV, dK, dQ) = 2.5x the forward;
+        # bytes: read Q, K, V, O, dO and LSE, write dQ, dK, dV
+        aflops, mflops = int(2.5 * aflops), int(2.5 * mflops)
+        abytes = acc.alg_bytes_bwd(w.B, w.H, w.N, w.d, elem)
+        metric = "attn bwd TFLOP/s (2.5 x 4·B·H·N²·d)"
+    R = 1 if args.warm_cache else max(1, math.ceil(ROTATE_BYTES / abytes))
+    sets = make_sets(torch, dev, w, R)
+    stream = torch.cuda.Stream()
+    grads = []
+    if args.impl == "fa1_order":
+        ws = torch.empty(fa.fa_fwd_fa1_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+    else:
+        ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+        for r, (q, k, v, o, lse) in enumerate(sets):
+            fa.fa_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.d, w.scale, w.causal)  # O, LSE (untimed)
+            do = inputs.make_like(q.cpu(), 1000 + r).to(dev)
+            grads.append((do, torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)))
+        torch.cuda.synchronize()
+
+    def launch(i):
+        q, k, v, o, lse = sets[i % R]
+        if args.impl == "fa1_order":
+            fa.fa_fwd_fa1_order(q, k, v, o, lse, ws, w.B, w.H, w.N, w.d, w.scale, w.causal)
+        else:
+            do, dq, dk, dv = grads[i % R]
+            fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, w.B, w.H, w.N, w.d, w.scale, w.causal)
+
+    out_t = sets[0][3] if args.impl != "bwd" else grads[0][1]
+    wall, kern, K, graph = run_timed(torch, stream, launch, args.steps, args.warmup, args.settle, args.eager,
+                                     check=lambda: out_t.clone())
+    rl = roofline(aflops, abytes, kern)
+    rl.update({"traffic": None, "kernel": {"fa1_order": "fa_fwd_fa1_kernel",
+                                           "bwd": "fa_bwd (dQ + dK/dV kernels)"}[args.impl],
+               "kernel_us": round(kern * 1e6, 3), "alg_bytes": abytes, "alg_flop": aflops})
+    log(f"{args.impl} {w.name}: kernel {kern*1e6:.2f} us; {aflops/kern/1e12:.1f} TFLOP/s alg")
+    print(json.dumps({
+        "metric": metric, "value": round(aflops / wall / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "input_sets": R, "graph": graph, "impl": args.impl},
+        "roofline": rl}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(inputs.WORKLOADS) + ["varlen_mix"])
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(inputs.WORKLOADS) + ["varlen_mix"],
+                    help="headline workload (default: the causal N=8192 d=128 head group)")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="time only the headline workload (no per-workload records)")
     ap.add_argument("--layout", default="bhnd", choices=["bhnd", "bnhd", "qkvpacked"],
                     help="tensor layout at the boundary (fa_fwd / fa_fwd_strided)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work in total")
     ap.add_argument("--eager", action="store_true", help="launch from Python each step (no graph)")
     ap.add_argument("--warm-cache", action="store_true", help="one input set (cache-resident)")
     ap.add_argument("--settle", type=float, default=0.5,
@@ -223,161 +469,67 @@ def main() -> int:
     if args.workload == "varlen_mix":
         return bench_varlen(args, torch, fa, dev)
     w = inputs.WORKLOADS[args.workload]
-    elem = 2
-    abytes = acc.alg_bytes(w.B, w.H, w.N, w.d, elem)
-    aflops = acc.alg_flops(w.B, w.H, w.N, w.d, w.causal)
-    mflops = acc.metric_flops(w.B, w.H, w.N, w.d)
-    metric = METRIC
-    if args.impl == "bwd":
-        # backward: five N x N x d products (S, dP, dV, dK, dQ) = 2.5x the forward;
-        # bytes: read Q, K, V, O, dO and LSE, write dQ, dK, dV
-        aflops, mflops = int(2.5 * aflops), int(2.5 * mflops)
-        abytes = acc.alg_bytes_bwd(w.B, w.H, w.N, w.d, elem)
-        metric = "attn bwd TFLOP/s (2.5 x 4·B·H·N²·d)"
-    R = 1 if args.warm_cache else max(1, math.ceil(ROTATE_BYTES / abytes))
-    log(f"workload {w.name}: {w.describe()}; {R} rotating input sets; alg bytes {abytes/1e6:.2f} MB, "
-        f"alg flop {aflops/1e9:.2f} G")
+    if args.impl != "fa2":
+        return bench_other_impl(args, torch, fa, dev, w)
 
-    sets = []
-    for r in range(R):
-        q, k, v = (t.to(dev) for t in inputs.make_workload(w, seed=r))
-        if args.layout == "bnhd":
-            q, k, v = (t.transpose(1, 2).contiguous() for t in (q, k, v))
-        elif args.layout == "qkvpacked":
-            qkv = torch.stack([t.transpose(1, 2) for t in (q, k, v)], dim=2).contiguous()
-            q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
-        o = torch.empty_like(q) if args.layout == "bhnd" else torch.empty(
-            (w.B, w.N, w.H, w.d), dtype=q.dtype, device=dev)
-        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
-        sets.append((q, k, v, o, lse))
     stream = torch.cuda.Stream()
-    ws = None
-    grads = []
-    if args.impl == "fa1_order":
-        ws = torch.empty(fa.fa_fwd_fa1_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
-    elif args.impl == "bwd":
-        ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
-        for r, (q, k, v, o, lse) in enumerate(sets):
-            fa.fa_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.d, w.scale, w.causal)  # O, LSE (untimed)
-            do = inputs.make_like(q.cpu(), 1000 + r).to(dev)
-            grads.append((do, torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)))
-        torch.cuda.synchronize()
+    log(f"headline {w.name}: {w.describe()}")
+    # the headline: exactly K timed steps (one replay of the K-launch graph)
+    head = bench_fwd_workload(torch, fa, dev, stream, w, args.steps, args.warmup, args.settle, args.eager,
+                              args.warm_cache, 0.0, args.layout)
+    wall, kern = head.pop("_wall"), head.pop("_kern")
+    graph = head.pop("_graph")
+    per_config = None
+    if not args.no_per_config and args.layout == "bhnd":
+        per_config = {}
+        for name in CONFIG_ORDER:
+            wc = inputs.WORKLOADS[name]
+            rec = bench_fwd_workload(torch, fa, dev, stream, wc, args.steps, args.warmup, args.settle,
+                                     args.eager, args.warm_cache, PER_CONFIG_MIN_S)
+            for key in ("_wall", "_kern", "_graph"):
+                rec.pop(key)
+            rec.update({"B": wc.B, "H": wc.H, "N": wc.N, "d": wc.d, "dtype": wc.dtype, "causal": wc.causal})
+            per_config[name] = rec
+    cgbs = copy_bandwidth(torch, dev, stream)
+    log(f"device copy {cgbs:.0f} GB/s")
 
-    def launch(i):
-        q, k, v, o, lse = sets[i % R]
-        if args.impl == "fa2" and args.layout != "bhnd":
-            st = fa._strides_bnhd
-            fa.fa_fwd_strided(q, k, v, o, lse, w.B, w.H, w.N, w.d, w.scale, w.causal,
-                              st(q), st(k), st(v), st(o))
-        elif args.impl == "fa2":
-            fa.fa_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.d, w.scale, w.causal)
-        elif args.impl == "fa1_order":
-            fa.fa_fwd_fa1_order(q, k, v, o, lse, ws, w.B, w.H, w.N, w.d, w.scale, w.causal)
-        else:
-            do, dq, dk, dv = grads[i % R]
-            fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, w.B, w.H, w.N, w.d, w.scale, w.causal)
-
-    with torch.cuda.stream(stream):
-        for i in range(args.warmup):
-            launch(i)
-    torch.cuda.synchronize()
-    out_idx = sets[0][3] if args.impl != "bwd" else grads[0][1]
-    ref_o = out_idx.clone()
-
-    K = args.steps
-    graph = None
-    if not args.eager:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            for i in range(K):
-                launch(i)
-        torch.cuda.synchronize()
-        graph.replay()  # untimed replay: check the graph reproduces the eager output
-        torch.cuda.synchronize()
-        if not torch.equal(out_idx, ref_o):
-            log("graph replay disagrees with the eager launch")
-            return 1
-
-    # untimed settle phase: the same steps until `settle` seconds have passed
-    t_set = time.perf_counter()
-    with torch.cuda.stream(stream):
-        while time.perf_counter() - t_set < args.settle:
-            if graph is not None:
-                graph.replay()
-            else:
-                for i in range(K):
-                    launch(i)
-            torch.cuda.synchronize()
-
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        ev0.record(stream)
-        if graph is not None:
-            graph.replay()
-        else:
-            for i in range(K):
-                launch(i)
-        ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ev_ms = ev0.elapsed_time(ev1)
-
-    ms_per_step = wall * 1e3 / K
-    kern_s = ev_ms * 1e-3 / K  # average launch duration on the launch stream
-    value = mflops / (ms_per_step * 1e-3) / 1e12
-    intensity = aflops / abytes
-    ridge = acc.MFMA_PEAK_TFLOPS_16BIT * 1e12 / (acc.HBM_PEAK_GBS * 1e9)
-    if intensity < ridge:
-        achieved, peak, unit, bound = abytes / kern_s / 1e9, acc.HBM_PEAK_GBS, "GB/s", "hbm"
-    else:
-        achieved, peak, unit, bound = aflops / kern_s / 1e12, acc.MFMA_PEAK_TFLOPS_16BIT, "TFLOP/s", "mfma"
-    log(f"ms/step {ms_per_step:.4f} (wall), kernel avg {kern_s*1e6:.2f} us (events); "
-        f"{aflops/kern_s/1e12:.1f} TFLOP/s alg, {abytes/kern_s/1e9:.0f} GB/s alg")
-
+    aflops = head["alg_flop"]
+    mflops = acc.metric_flops(w.B, w.H, w.N, w.d)
+    rl = dict(head["roofline"])
+    rl.update({"kernel": "fa_fwd", "kernel_us": head["kernel_us"], "alg_bytes": head["alg_bytes"],
+               "alg_flop": aflops, "copy_gbs": round(cgbs, 1)})
+    if rl["bound"] == "hbm":
+        rl["frac_of_copy"] = round(rl["achieved"] / cgbs, 4)
+    if w.causal:
+        rl["note"] = ("value and achieved count only the computed pairs j <= i, 4·B·H·d·N(N+1)/2; the "
+                      "metric's literal 4·B·H·N²·d counts the masked half too (value_literal_formula)")
     out = {
-        "metric": metric,
-        "value": round(value, 3),
+        "metric": METRIC,
+        "value": round(aflops / wall / 1e12, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(wall * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
-                   "input_sets": R, "graph": graph is not None, "impl": args.impl, "layout": args.layout,
-                   "settle_s": args.settle,
-                   "parallelism": "none (1 GPU)"},
-        "roofline": {
-            "bound": bound,
-            "achieved": round(achieved, 2),
-            "peak": peak,
-            "unit": unit,
-            "frac": round(achieved / peak, 4),
-            "traffic": stored_traffic(w.name) if args.impl == "fa2" else None,
-            "kernel": {"fa2": "fa_fwd", "fa1_order": "fa_fwd_fa1_kernel",
-                       "bwd": "fa_bwd (dot + dK/dV + dQ kernels)"}[args.impl],
-            "kernel_us": round(kern_s * 1e6, 3),
-            "alg_bytes": abytes,
-            "alg_flop": aflops,
-        },
+                   "sigma_qk": w.sigma_qk, "input_sets": head["input_sets"], "graph": graph,
+                   "layout": args.layout, "settle_s": args.settle, "parallelism": "none (1 GPU)"},
+        "roofline": rl,
     }
     if w.causal:
-        out["roofline"]["note"] = ("value uses the metric's 4·B·H·N²·d, which counts the masked "
-                                   "half of a causal problem; achieved counts only the computed half")
-    if bound == "hbm":
-        # the rate a plain copy reaches on this GPU, timed in the same run
-        cgbs = copy_bandwidth(torch, dev, stream)
-        out["roofline"]["copy_gbs"] = round(cgbs, 1)
-        out["roofline"]["frac_of_copy"] = round(achieved / cgbs, 4)
-        log(f"device copy {cgbs:.0f} GB/s; kernel reaches {achieved / cgbs:.1%} of it")
+        out["value_literal_formula"] = round(mflops / wall / 1e12, 3)
+    if per_config is not None:
+        for rec in per_config.values():
+            if rec["roofline"]["bound"] == "hbm":
+                rec["roofline"]["frac_of_copy"] = round(rec["roofline"]["achieved"] / cgbs, 4)
+        out["per_config"] = per_config
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, per_config is not None)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -96,10 +96,41 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _contiguous(**ts) -> None:
+    for name, t in ts.items():
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous (the kernels read it as a dense row-major tensor)")
+
+
+def _need(t, name: str, numel: int, dtype=None) -> None:
+    """A dense tensor holding at least `numel` elements (of `dtype`), so that the
+    kernel's reads and writes stay inside it."""
+    if t is None:
+        return
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements; the call needs {numel}")
+
+
+def _check_lse(lse, B: int, H: int, N: int, q) -> None:
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, H, N):
+        raise ValueError(f"lse must be a contiguous float32 tensor of shape {(B, H, N)}, got "
+                         f"{lse.dtype} {tuple(lse.shape)} (contiguous={lse.is_contiguous()})")
+    if lse.device != q.device:
+        raise ValueError("lse must live on q's device")
+
+
 # ---------------------------------------------------------------------------
 # raw entry points (same names and argument order as the C ABI)
 # ---------------------------------------------------------------------------
 def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream=None):
+    n = B * H * N * d
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _need(t, name, n)
+    _need(lse, "lse", B * H * N, torch.float32)
     _dev(q, k, v, o, lse)
     _check(lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                         float(scale), int(bool(causal)), _dtype_code(q), _stream(stream)), "fa_fwd")
@@ -107,6 +138,7 @@ def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream=None):
 
 def fa_fwd_strided(q, k, v, o, lse, B, H, N, d, scale, causal, q_strides, k_strides, v_strides,
                    o_strides, stream=None):
+    _need(lse, "lse", B * H * N, torch.float32)
     _dev(q, k, v, o, lse)
     _check(lib().fa_fwd_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                                 float(scale), int(bool(causal)), _dtype_code(q),
@@ -115,6 +147,10 @@ def fa_fwd_strided(q, k, v, o, lse, B, H, N, d, scale, causal, q_strides, k_stri
 
 
 def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, T, max_seqlen, H, d, scale, causal, stream=None):
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _need(t, name, T * H * d)
+    _need(lse, "lse", H * T, torch.float32)
+    _need(cu_seqlens, "cu_seqlens", B + 1, torch.int32)
     _dev(q, k, v, o, lse, cu_seqlens)
     _check(lib().fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens), B, T,
                                max_seqlen, H, d, float(scale), int(bool(causal)), _dtype_code(q),
@@ -122,6 +158,10 @@ def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, T, max_seqlen, H, d, scale, ca
 
 
 def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, workspace, B, H, N, d, scale, causal, stream=None):
+    n = B * H * N * d
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _need(t, name, n)
+    _need(lse, "lse", B * H * N, torch.float32)
     _dev(q, k, v, o, do, lse, dq, dk, dv, workspace)
     _check(lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
                         _ptr(dv), _ptr(workspace), B, H, N, d, float(scale), int(bool(causal)),
@@ -133,6 +173,10 @@ def fa_bwd_workspace_bytes(B, H, N, d) -> int:
 
 
 def fa_fwd_fa1_order(q, k, v, o, lse, workspace, B, H, N, d, scale, causal, stream=None):
+    n = B * H * N * d
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _need(t, name, n)
+    _need(lse, "lse", B * H * N, torch.float32)
     _dev(q, k, v, o, lse, workspace)
     _check(lib().fa_fwd_fa1_order(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace), B, H,
                                   N, d, float(scale), int(bool(causal)), _dtype_code(q),
@@ -162,7 +206,7 @@ def attention(q, k, v, causal=False, scale=None, stream=None):
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
         raise ValueError("q, k, v must be contiguous [B, H, N, d]")
     B, H, N, d = q.shape
-    o = torch.empty_like(q)
+    o = torch.empty_like(q, memory_format=torch.contiguous_format)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     fa_fwd(q, k, v, o, lse, B, H, N, d, _default_scale(d, scale), causal, stream)
     return o, lse
@@ -199,11 +243,14 @@ def attention_qkvpacked(qkv, causal=False, scale=None, stream=None):
 def attention_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, stream=None):
     """O [T, H, d] and LSE [H, T] for packed sequences q, k, v of shape [T, H, d]."""
     _same(q, k, v)
+    _contiguous(q=q, k=k, v=v)
     T, H, d = q.shape
     if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous():
         raise ValueError("cu_seqlens must be a contiguous int32 tensor")
+    if cu_seqlens.device != q.device:
+        raise ValueError("cu_seqlens must live on q's device")
     B = cu_seqlens.numel() - 1
-    o = torch.empty_like(q)
+    o = torch.empty_like(q, memory_format=torch.contiguous_format)
     lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
     fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, T, int(max_seqlen), H, d,
                   _default_scale(d, scale), causal, stream)
@@ -213,8 +260,10 @@ def attention_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, 
 def attention_backward(q, k, v, o, lse, do, causal=False, scale=None, stream=None):
     """dq, dk, dv for contiguous [B, H, N, d] tensors and the forward's LSE."""
     _same(q, k, v, o, do)
+    _contiguous(q=q, k=k, v=v, o=o, do=do)
     B, H, N, d = q.shape
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    _check_lse(lse, B, H, N, q)
+    dq, dk, dv = (torch.empty_like(t, memory_format=torch.contiguous_format) for t in (q, k, v))
     ws = torch.empty(max(fa_bwd_workspace_bytes(B, H, N, d), 16), dtype=torch.uint8, device=q.device)
     fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, B, H, N, d, _default_scale(d, scale), causal, stream)
     return dq, dk, dv
@@ -223,8 +272,9 @@ def attention_backward(q, k, v, o, lse, do, causal=False, scale=None, stream=Non
 def attention_fa1_order(q, k, v, causal=False, scale=None, stream=None):
     """The FlashAttention-1 loop order (ablation); same result as ``attention``."""
     _same(q, k, v)
+    _contiguous(q=q, k=k, v=v)
     B, H, N, d = q.shape
-    o = torch.empty_like(q)
+    o = torch.empty_like(q, memory_format=torch.contiguous_format)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     ws = torch.empty(max(fa_fwd_fa1_workspace_bytes(B, H, N, d), 16), dtype=torch.uint8, device=q.device)
     fa_fwd_fa1_order(q, k, v, o, lse, ws, B, H, N, d, _default_scale(d, scale), causal, stream)

@@ -34,6 +34,29 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
   return x < y + static_cast<uintptr_t>(nb) && y < x + static_cast<uintptr_t>(na);
 }
 
+// True when the rows (b, h, i) of a strided [B, H, N, d] tensor share no
+// element: with the axes of extent above 1 sorted by stride, each stride must
+// reach past everything the smaller axes span (a row spans d elements). This
+// is sufficient; layouts it rejects would have several workgroups write the
+// same bytes of an output.
+bool rows_disjoint(int64_t sb, int64_t sh, int64_t sr, int B, int H, int N, int d) {
+  int64_t ax[3][2] = {{sr, N}, {sh, H}, {sb, B}};
+  for (int i = 0; i < 3; ++i)  // insertion sort by stride
+    for (int j = i; j > 0 && ax[j][0] < ax[j - 1][0]; --j)
+      for (int c = 0; c < 2; ++c) {
+        const int64_t t = ax[j][c];
+        ax[j][c] = ax[j - 1][c];
+        ax[j - 1][c] = t;
+      }
+  int64_t reach = d;
+  for (int i = 0; i < 3; ++i) {
+    if (ax[i][1] <= 1) continue;
+    if (ax[i][0] < reach) return false;
+    reach += ax[i][0] * (ax[i][1] - 1);  // no overflow: bounded by the span check
+  }
+  return true;
+}
+
 // Common checks of (B, H, N, d, scale, dtype); returns FA_OK or an error and
 // the element count B*H*N*d in *elems.
 int check_problem(int B, int H, int N, int d, float scale, int dtype, int64_t* elems) {
@@ -109,7 +132,7 @@ const char* fa_strerror(int code) {
     case FA_ERR_SCALE: return "scale is not finite";
     case FA_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
     case FA_ERR_LAUNCH: return "kernel launch failed";
-    case FA_ERR_ALIAS: return "an output overlaps an input";
+    case FA_ERR_ALIAS: return "an output overlaps an input, the other output or itself";
     case FA_ERR_DEVICE: return "current device is not a usable gfx950";
     default: return "unknown fa_status";
   }
@@ -155,8 +178,10 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
     if (i % 3 == 2 && st[i] > kMaxRowStride) return FA_ERR_DIM;
     if (st[i] % 8) return FA_ERR_ALIGN;
   }
-  // the largest element offset reached must stay addressable
+  // the largest element offset reached must stay addressable; span[t] is the
+  // element count from a tensor's base to just past its last element
   const int64_t ext[3] = {B, H, N};
+  int64_t span[4];
   for (int t = 0; t < 4; ++t) {
     int64_t far = d, x = 0;
     for (int i = 0; i < 3; ++i) {
@@ -164,11 +189,19 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
       far += x;
       if (far >= (INT64_C(1) << 62)) return FA_ERR_DIM;
     }
+    span[t] = far;
   }
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       (reinterpret_cast<uintptr_t>(lse) & 3))
     return FA_ERR_ALIGN;
-  if (o == q || o == k || o == v) return FA_ERR_ALIAS;
+  // o's and lse's address ranges must not meet q's, k's or v's, nor each other
+  const void* in[3] = {q, k, v};
+  const int64_t lbytes = elems / d * 4;
+  for (int t = 0; t < 3; ++t)
+    if (overlap(o, span[3] * 2, in[t], span[t] * 2) || overlap(lse, lbytes, in[t], span[t] * 2))
+      return FA_ERR_ALIAS;
+  if (overlap(lse, lbytes, o, span[3] * 2)) return FA_ERR_ALIAS;
+  if (!rows_disjoint(o_sb, o_sh, o_sr, B, H, N, d)) return FA_ERR_ALIAS;
   if ((rc = device_ok()) != FA_OK) return rc;
 
   FwdArgs a{};

@@ -14,6 +14,8 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out);
 bool head_dim_ok(int d);
 bool aligned16(const void* p);
 bool overlap(const void* a, int64_t na, const void* b, int64_t nb);
+// the rows of a strided [B, H, N, d] tensor share no element
+bool rows_disjoint(int64_t sb, int64_t sh, int64_t sr, int B, int H, int N, int d);
 // checks of (B, H, N, d, scale, dtype); *elems = B*H*N*d on success
 int check_problem(int B, int H, int N, int d, float scale, int dtype, int64_t* elems);
 // FA_OK when the current device is a gfx950 (cached per device)

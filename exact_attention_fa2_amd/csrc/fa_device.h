@@ -86,6 +86,16 @@ __device__ __forceinline__ float xor_lane32(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+// Orders this wave's LDS writes before its later LDS reads of what other
+// lanes wrote (wave-scope release/acquire; the LDS executes one wave's
+// operations in order, so no wait instruction is needed, only that the
+// compiler keeps the order).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ bool wave_any(bool p) {
   return __builtin_amdgcn_ballot_w64(p) != 0;
 }

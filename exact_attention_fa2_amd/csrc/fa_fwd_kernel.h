@@ -532,6 +532,7 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(const FwdArgs a) {
     const int qrow = qw0 + 32 * j + l32;
     if (hh == 0 && qrow < Nb) Lg[qrow] = (m_run[j] + fast_log2(l_lse)) * kLn2;
   }
+  wave_lds_sync();  // the rows below were written by other lanes of this wave
   constexpr int CPR = D / 8;  // 16-byte chunks per output row
 #pragma unroll
   for (int i = 0; i < QW * CPR / 64; ++i) {

@@ -33,6 +33,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// s_waitcnt lgkmcnt(0) with vmcnt and expcnt left at their maxima: every LDS
+// read this wave has issued has returned.
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 template <int D, int NS, int NB>
 struct SplitSmem {
   static constexpr int BC = 64;
@@ -149,9 +153,16 @@ __global__ __launch_bounds__(NS * 64) void fa_fwd_split_kernel(const FwdArgs a) 
       tile_step_fwd<D, DT, CAUSAL, 1, BC, 0, 0, PF>(t == t_begin, need_mask, wl + buf * SM::TILE,
                                                     wl + (NB + buf) * SM::TILE, key0, Nb, qw0, lane, a.c, qf,
                                                     oacc, m_run, l_run);
-      // one buffer: the next tile's loads wait until this tile's LDS reads
-      // are done (the MFMAs that consumed them have been issued)
-      if (NB == 1 && t + 1 < t_end) dma(t + 1, 0);
+      // one buffer: the next tile's DMA writes the buffer this tile has just
+      // read, so it waits until those LDS reads have returned (lgkmcnt 0),
+      // and the fences keep the compiler from moving the reads below the wait or
+      // the DMA above it
+      if (NB == 1 && t + 1 < t_end) {
+        __builtin_amdgcn_sched_barrier(0);
+        wait_lgkmcnt0();
+        __builtin_amdgcn_sched_barrier(0);
+        dma(t + 1, 0);
+      }
     }
   }
 
@@ -213,6 +224,7 @@ __global__ __launch_bounds__(NS * 64) void fa_fwd_split_kernel(const FwdArgs a) 
       x[1] = pack2<DT>(oacc[0][db][4 * g4 + 2] * inv, oacc[0][db][4 * g4 + 3] * inv);
       *(u32x2*)(ob + l32 * OSTR + db * 32 + 8 * g4 + 4 * hh) = x;
     }
+  wave_lds_sync();  // the rows below were written by other lanes of this wave
   const int qrow = qw0 + l32;
   if (hh == 0 && qrow < Nb) Lg[qrow] = (m + fast_log2(l_lse)) * kLn2;
 #pragma unroll

@@ -55,7 +55,7 @@ typedef enum {
   FA_ERR_SCALE = -4,       /* scale is NaN or infinite                          */
   FA_ERR_ALIGN = -5,       /* pointer or row stride not 16-byte aligned         */
   FA_ERR_LAUNCH = -6,      /* the HIP launch itself failed                      */
-  FA_ERR_ALIAS = -7,       /* an output buffer overlaps an input buffer         */
+  FA_ERR_ALIAS = -7,       /* an output overlaps an input, the other output or itself */
   FA_ERR_DEVICE = -8       /* no usable gfx950 device is current                */
 } fa_status;
 
@@ -89,7 +89,12 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
  *                      and head strides must be multiples of 8 elements;
  *                      row strides at most 2^24 elements (FA_ERR_DIM beyond).
  *   lse     : [B, H, N] fp32 contiguous.
- * Overlap of o with q/k/v is only checked for identical base pointers.
+ * The address ranges of o and lse (from the base pointer to the last element
+ * the strides reach) must not meet those of q, k or v, nor each other, and no
+ * two rows of o may share an element (with o's axes of extent above 1 sorted
+ * by stride, each stride must reach past what the smaller axes span; a row
+ * spans d elements): FA_ERR_ALIAS otherwise. q, k and v may share memory, as
+ * in a packed QKV tensor.
  */
 int fa_fwd_strided(const void *q, const void *k, const void *v, void *o, float *lse,
                    int B, int H, int N, int d, float scale, int causal, int dtype,

@@ -1,10 +1,16 @@
 """Shared helpers for the GPU parity tests: run the HIP path, run the oracle on
 the very same input bits, and apply the tolerance gate.
 
-Gate for O (fp16 / bf16 outputs): |O_gpu - O_ref| <= atol + ulp(O_ref)/2, with
-atol = 2e-3 (fp16) or 1e-2 (bf16) and ulp the spacing of the output dtype at
-|O_ref| (rounding the exact result to the output dtype alone may cost half an
-ulp, which exceeds atol for bf16 once |O| >= 2). LSE: |LSE_gpu - LSE_ref| <= 1e-3.
+Gate for O, elementwise against the fp64 oracle:
+  * fp16: |O_gpu - O_ref| <= 2e-3, the stated max-abs tolerance, at every
+    magnitude.
+  * bf16: |O_gpu - O_ref| <= 1e-2 wherever half a bf16 ulp of O_ref is at most
+    1e-2 (|O_ref| < 4); where it is larger, 1e-2 + ulp(O_ref)/2. Rounding the
+    exact result to bf16 alone costs up to half an ulp, 2^-6 = 0.0156 for
+    |O| in [4, 8), which the long causal workload's large-logit rows reach.
+LSE: |LSE_gpu - LSE_ref| <= 1e-3.
+Every gate returns the raw max-abs error; gate_o also reports whether the
+plain max-abs bound (no ulp allowance) held.
 """
 from __future__ import annotations
 
@@ -28,16 +34,31 @@ def ulp(x: np.ndarray, dtype: str) -> np.ndarray:
     return np.exp2(e - MANT[dtype])
 
 
+def o_bound(o_ref: np.ndarray, dtype: str) -> np.ndarray:
+    """Per-element bound on |O_gpu - O_ref| (see the module docstring)."""
+    atol = ATOL[dtype]
+    if dtype == "f16":
+        return np.full(np.shape(o_ref), atol)
+    half = 0.5 * ulp(o_ref, dtype)
+    return np.where(half > atol, atol + half, atol)
+
+
+LAST_STRICT = {"held": True, "max_abs": 0.0}
+
+
 def gate_o(o_gpu: np.ndarray, o_ref: np.ndarray, dtype: str, what: str = "O") -> float:
     o_gpu = np.asarray(o_gpu, np.float64)
     err = np.abs(o_gpu - o_ref)
-    bound = ATOL[dtype] + 0.5 * ulp(o_ref, dtype)
+    bound = o_bound(o_ref, dtype)
     bad = ~(err <= bound)
     if bad.any():
         i = np.unravel_index(np.argmax(np.where(bad, err - bound, -np.inf)), err.shape)
         raise AssertionError(f"{what}: {int(bad.sum())} of {err.size} outside the gate; worst at {i}: "
                              f"gpu={o_gpu[i]!r} ref={o_ref[i]!r} err={err[i]:.3e} bound={bound[i]:.3e}")
-    return float(err.max()) if err.size else 0.0
+    mx = float(err.max()) if err.size else 0.0
+    LAST_STRICT["held"] = mx <= ATOL[dtype]
+    LAST_STRICT["max_abs"] = mx
+    return mx
 
 
 def gate_lse(lse_gpu: np.ndarray, lse_ref: np.ndarray) -> float:

@@ -116,6 +116,29 @@ def test_strided_argument_errors(L):
     assert strided(L, d=32) == UNSUP
 
 
+def test_strided_overlap_errors(L):
+    s = [64 * 8 * 64, 64, 8 * 64] * 4  # [B, N, H, d] strides, B=2 H=8 N=64 d=64
+    span = 2 * 64 * 8 * 64 * 2  # bytes of one such tensor
+    assert strided(L) == OK or strided(L) == DEVICE  # a valid call (no GPU here)
+    assert strided(L, o=A + span - 16) == ALIAS           # o starts inside q's range
+    assert strided(L, lse=A + 64 * MB + 64) == ALIAS      # lse inside k
+    assert strided(L, lse=A + 192 * MB + 4) == ALIAS      # lse inside o
+    # packed QKV: q, k, v interleaved in one buffer are legal inputs
+    pk = [64 * 3 * 8 * 64, 64, 3 * 8 * 64] * 3 + [64 * 8 * 64, 64, 8 * 64]
+    assert strided(L, pk, k=A + 8 * 64 * 2, v=A + 2 * 8 * 64 * 2) in (OK, DEVICE)
+    # output rows that collide
+    for o_st in ([64 * 8 * 64, 64, 32],          # row stride below a row's 64 elements
+                 [64 * 8 * 64, 0, 8 * 64],       # head stride 0 with 8 heads
+                 [0, 64, 8 * 64],                # batch stride 0 with 2 batches
+                 [64 * 8 * 64, 64, 8 * 8]):      # rows of consecutive heads interleave
+        bad = s[:9] + o_st
+        assert strided(L, bad) == ALIAS, o_st
+    # rows that only touch (no shared element) are fine: o as [B, H, N, d]
+    assert strided(L, s[:9] + [8 * 64 * 64, 64 * 64, 64]) in (OK, DEVICE)
+    # an axis of extent 1 may have any stride
+    assert strided(L, s[:9] + [0, 64, 8 * 64], B=1) in (OK, DEVICE)
+
+
 def test_varlen_argument_errors(L):
     def call(**kw):
         a = dict(q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 256 * MB, cu=A + 300 * MB,
@@ -181,3 +204,42 @@ def test_bwd_argument_errors(L):
     assert L.fa_bwd_workspace_bytes(2, 3, 100, 64) >= 2 * 3 * 100 * 4
     assert L.fa_bwd_workspace_bytes(2, 3, 0, 64) == 0
     assert L.fa_bwd_workspace_bytes(2, 3, 100, 70) == -1
+
+
+def test_python_wrappers_check_layout_before_any_gpu_call(L):
+    # every check below raises on CPU tensors before the device check, so it
+    # would equally stop a bad call before any GPU work
+    import torch
+    B, H, N, d = 1, 2, 16, 64
+    q = torch.zeros(B, H, N, d, dtype=torch.float16)
+    bnhd = torch.zeros(B, N, H, d, dtype=torch.float16).transpose(1, 2)  # [B, H, N, d] view, not dense
+    lse = torch.zeros(B, H, N, dtype=torch.float32)
+    with pytest.raises(ValueError, match="contiguous"):
+        fa.attention_backward(q, q, q, bnhd, lse, q)
+    with pytest.raises(ValueError, match="contiguous"):
+        fa.attention_backward(q, q, q, q, lse, bnhd)
+    for bad in (lse.half(), lse.double(), torch.zeros(B, H, N - 1), torch.zeros(B, H, 2 * N)[..., ::2]):
+        with pytest.raises(ValueError, match="lse"):
+            fa.attention_backward(q, q, q, q, bad, q)
+    with pytest.raises(ValueError, match="contiguous"):
+        fa.attention_fa1_order(bnhd, bnhd, bnhd)
+    T = 16
+    qt = torch.zeros(T, H, d, dtype=torch.float16)
+    cu = torch.tensor([0, T], dtype=torch.int32)
+    with pytest.raises(ValueError, match="contiguous"):
+        fa.attention_varlen(qt, torch.zeros(H, T, d, dtype=torch.float16).transpose(0, 1), qt, cu, T)
+    # the raw entry points check element counts and the fp32 LSE
+    o = torch.empty_like(q)
+    with pytest.raises(ValueError, match="lse"):
+        fa.fa_fwd(q, q, q, o, lse.half(), B, H, N, d, 0.125, False)
+    with pytest.raises(ValueError, match="elements"):
+        fa.fa_fwd(q, q, q, o, lse, B, H, 2 * N, d, 0.125, False)
+    with pytest.raises(ValueError, match="contiguous"):
+        fa.fa_fwd(q, q, q, bnhd, lse, B, H, N, d, 0.125, False)
+    with pytest.raises(ValueError, match="elements"):
+        fa.fa_bwd(q, q, q, q, q, lse, q, q, q, None, B, H, N + 1, d, 0.125, False)
+    with pytest.raises(ValueError, match="cu_seqlens"):
+        fa.fa_fwd_varlen(qt, qt, qt, qt, torch.zeros(H, T), cu.long(), 1, T, T, H, d, 0.125, False)
+    # outputs of the wrappers are dense whatever the inputs' memory format
+    x = torch.zeros(1, 2, 4, 64, dtype=torch.float16).to(memory_format=torch.channels_last)
+    assert not x.is_contiguous() and torch.empty_like(x, memory_format=torch.contiguous_format).is_contiguous()
