@@ -7,7 +7,7 @@ turns negative status codes into exceptions. There is no fallback: if the
 library is missing or the tensors are not on a gfx950 device the calls fail.
 
 Names follow the C ABI: ``fa_fwd``, ``fa_fwd_strided``, ``fa_fwd_varlen``,
-``fa_bwd``, ``fa_fwd_fa1_order``. Convenience wrappers that allocate the
+``fa_bwd``, ``fa_bwd_noalloc``, ``fa_fwd_fa1_order``. Convenience wrappers that allocate the
 outputs: ``attention``, ``attention_bnhd``, ``attention_qkvpacked``,
 ``attention_varlen``, ``attention_backward``.
 """
@@ -25,8 +25,9 @@ FA_F16, FA_BF16 = 0, 1
 STATUS = {
     0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_DIM", -3: "FA_ERR_UNSUPPORTED",
     -4: "FA_ERR_SCALE", -5: "FA_ERR_ALIGN", -6: "FA_ERR_LAUNCH", -7: "FA_ERR_ALIAS",
-    -8: "FA_ERR_DEVICE",
+    -8: "FA_ERR_DEVICE", -9: "FA_ERR_TOO_LARGE",
 }
+BWD_NOALLOC_MAX_ROWS = 4194304  # FA_BWD_NOALLOC_MAX_ROWS of fa.h
 
 _lib = None
 _P = ctypes.c_void_p
@@ -40,6 +41,7 @@ _SIGS = {
     "fa_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
     "fa_bwd": (_I, [_P] * 10 + [_I, _I, _I, _I, _F, _I, _I, _P]),
     "fa_bwd_workspace_bytes": (_L, [_I, _I, _I, _I]),
+    "fa_bwd_noalloc": (_I, [_P] * 9 + [_I, _I, _I, _I, _F, _I, _I, _P]),
     "fa_fwd_fa1_order": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P]),
     "fa_fwd_fa1_workspace_bytes": (_L, [_I, _I, _I, _I]),
     "fa_strerror": (ctypes.c_char_p, [_I]),
@@ -166,6 +168,17 @@ def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, workspace, B, H, N, d, scale, causal
     _check(lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
                         _ptr(dv), _ptr(workspace), B, H, N, d, float(scale), int(bool(causal)),
                         _dtype_code(q), _stream(stream)), "fa_bwd")
+
+
+def fa_bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, B, H, N, d, scale, causal, stream=None):
+    n = B * H * N * d
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _need(t, name, n)
+    _need(lse, "lse", B * H * N, torch.float32)
+    _dev(q, k, v, o, do, lse, dq, dk, dv)
+    _check(lib().fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                                _ptr(dv), B, H, N, d, float(scale), int(bool(causal)), _dtype_code(q),
+                                _stream(stream)), "fa_bwd_noalloc")
 
 
 def fa_bwd_workspace_bytes(B, H, N, d) -> int:

@@ -134,6 +134,7 @@ const char* fa_strerror(int code) {
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_ALIAS: return "an output overlaps an input, the other output or itself";
     case FA_ERR_DEVICE: return "current device is not a usable gfx950";
+    case FA_ERR_TOO_LARGE: return "B*H*N exceeds the static scratch of fa_bwd_noalloc (FA_BWD_NOALLOC_MAX_ROWS)";
     default: return "unknown fa_status";
   }
 }

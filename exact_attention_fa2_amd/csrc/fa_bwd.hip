@@ -1,7 +1,9 @@
 // C ABI of the backward pass (fa_bwd, fa_bwd_workspace_bytes).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_bwd_kernel.h"
@@ -84,32 +86,68 @@ int64_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
   return bwd_bytes(B, H, N);
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* do_, const float* lse,
-           void* dq, void* dk, void* dv, void* workspace, int B, int H, int N, int d, float scale,
-           int causal, int dtype, void* stream) {
-  int64_t elems = 0;
-  int rc = check_problem(B, H, N, d, scale, dtype, &elems);
+}  // extern "C"
+
+// Scratch of fa_bwd_noalloc: the fp32 row terms D_i of at most
+// FA_BWD_NOALLOC_MAX_ROWS rows (B*H*N), 16 MiB. Each device holds its own
+// copy for the life of the process. Host code never passes `scratch` itself
+// (a host-side stand-in): it takes the device address from
+// hipGetSymbolAddress, once per device.
+static __device__ __align__(256) float scratch[FA_BWD_NOALLOC_MAX_ROWS];
+
+namespace fa {
+namespace {
+
+// Device address of this device's `scratch`, looked up on the first call on
+// each device (that device current) and kept; nullptr if the lookup fails.
+void* scratch_address() {
+  static std::atomic<void*> addr[64];
+  static std::mutex mu;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(mu);
+  p = addr[dev].load(std::memory_order_relaxed);
+  if (p) return p;
+  void* q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return nullptr;
+  addr[dev].store(q, std::memory_order_release);
+  return q;
+}
+
+// Checks shared by fa_bwd and fa_bwd_noalloc (everything but the workspace).
+// max_rows > 0 bounds B*H*N (FA_ERR_TOO_LARGE), checked with the sizes,
+// before any pointer.
+int check_bwd(const void* q, const void* k, const void* v, const void* o, const void* do_, const float* lse,
+              void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int dtype,
+              int64_t max_rows, int64_t* elems) {
+  int rc = check_problem(B, H, N, d, scale, dtype, elems);
   if (rc != FA_OK) return rc;
   if (d == 256) return FA_ERR_UNSUPPORTED;
-  if (elems == 0) return FA_OK;
-  if (!q || !k || !v || !o || !do_ || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
+  if (*elems == 0) return FA_OK;
+  if (max_rows > 0 && *elems / d > max_rows) return FA_ERR_TOO_LARGE;
+  if (!q || !k || !v || !o || !do_ || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
   const void* a16[8] = {q, k, v, o, do_, dq, dk, dv};
   for (const void* p : a16)
     if (!aligned16(p)) return FA_ERR_ALIGN;
-  if (!aligned16(workspace) || (reinterpret_cast<uintptr_t>(lse) & 3)) return FA_ERR_ALIGN;
-  const int64_t nb = elems * 2, lb = (elems / d) * 4, wb = bwd_bytes(B, H, N);
+  if (reinterpret_cast<uintptr_t>(lse) & 3) return FA_ERR_ALIGN;
+  const int64_t nb = *elems * 2, lb = (*elems / d) * 4;
   const void* ins[6] = {q, k, v, o, do_, lse};
   const int64_t insz[6] = {nb, nb, nb, nb, nb, lb};
-  void* outs[4] = {dq, dk, dv, workspace};
-  const int64_t outsz[4] = {nb, nb, nb, wb};
-  for (int i = 0; i < 4; ++i) {
+  void* outs[3] = {dq, dk, dv};
+  for (int i = 0; i < 3; ++i) {
     for (int j = 0; j < 6; ++j)
-      if (overlap(outs[i], outsz[i], ins[j], insz[j])) return FA_ERR_ALIAS;
-    for (int j = i + 1; j < 4; ++j)
-      if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return FA_ERR_ALIAS;
+      if (overlap(outs[i], nb, ins[j], insz[j])) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], nb, outs[j], nb)) return FA_ERR_ALIAS;
   }
-  if ((rc = device_ok()) != FA_OK) return rc;
+  return FA_OK;
+}
 
+int run_bwd(const void* q, const void* k, const void* v, const void* o, const void* do_, const float* lse,
+            void* dq, void* dk, void* dv, float* dvec, int B, int H, int N, int d, float scale, int causal,
+            int dtype, void* stream) {
   BwdArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -120,7 +158,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   a.dq = static_cast<uint16_t*>(dq);
   a.dk = static_cast<uint16_t*>(dk);
   a.dv = static_cast<uint16_t*>(dv);
-  a.dvec = static_cast<float*>(workspace);
+  a.dvec = dvec;
   a.B = B;
   a.H = H;
   a.N = N;
@@ -129,6 +167,44 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   a.qsign = scale < 0.f ? 0x80008000u : 0u;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   return dtype == FA_BF16 ? pick_d<DT_BF16>(a, d, causal != 0, st) : pick_d<DT_F16>(a, d, causal != 0, st);
+}
+
+}  // namespace
+}  // namespace fa
+
+extern "C" {
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* do_, const float* lse,
+           void* dq, void* dk, void* dv, void* workspace, int B, int H, int N, int d, float scale,
+           int causal, int dtype, void* stream) {
+  int64_t elems = 0;
+  int rc = check_bwd(q, k, v, o, do_, lse, dq, dk, dv, B, H, N, d, scale, dtype, 0, &elems);
+  if (rc != FA_OK || elems == 0) return rc;
+  if (!workspace) return FA_ERR_NULL;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  const int64_t nb = elems * 2, lb = (elems / d) * 4, wb = bwd_bytes(B, H, N);
+  const void* other[9] = {q, k, v, o, do_, dq, dk, dv, lse};
+  for (int j = 0; j < 9; ++j)
+    if (overlap(workspace, wb, other[j], j == 8 ? lb : nb)) return FA_ERR_ALIAS;
+  if ((rc = device_ok()) != FA_OK) return rc;
+  return run_bwd(q, k, v, o, do_, lse, dq, dk, dv, static_cast<float*>(workspace), B, H, N, d, scale, causal,
+                 dtype, stream);
+}
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* do_,
+                   const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                   int causal, int dtype, void* stream) {
+  int64_t elems = 0;
+  int rc = check_bwd(q, k, v, o, do_, lse, dq, dk, dv, B, H, N, d, scale, dtype, FA_BWD_NOALLOC_MAX_ROWS,
+                     &elems);
+  if (rc != FA_OK || elems == 0) return rc;
+  if ((rc = device_ok()) != FA_OK) return rc;
+  void* ws = scratch_address();
+  if (ws == nullptr) return FA_ERR_DEVICE;
+  // every D_i the kernels read is written first in the same call, so the
+  // previous call's contents need no clearing
+  return run_bwd(q, k, v, o, do_, lse, dq, dk, dv, static_cast<float*>(ws), B, H, N, d, scale, causal, dtype,
+                 stream);
 }
 
 }  // extern "C"

@@ -56,7 +56,8 @@ typedef enum {
   FA_ERR_ALIGN = -5,       /* pointer or row stride not 16-byte aligned         */
   FA_ERR_LAUNCH = -6,      /* the HIP launch itself failed                      */
   FA_ERR_ALIAS = -7,       /* an output overlaps an input, the other output or itself */
-  FA_ERR_DEVICE = -8       /* no usable gfx950 device is current                */
+  FA_ERR_DEVICE = -8,      /* no usable gfx950 device is current                */
+  FA_ERR_TOO_LARGE = -9    /* the problem exceeds fa_bwd_noalloc's static scratch */
 } fa_status;
 
 /*
@@ -148,6 +149,29 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
 /* Bytes of workspace fa_bwd needs for this problem (0 when any size is 0;
  * -1 on invalid sizes). Host-only; makes no HIP call. */
 int64_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * fa_bwd_noalloc -- fa_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments and results as fa_bwd, without the
+ * workspace. The row terms D_i live instead in a static device array of the
+ * library (FA_BWD_NOALLOC_MAX_ROWS fp32 values, 16 MiB, held by each device
+ * the library runs on until the process ends). The call makes no hipMalloc or
+ * hipFree and calls no allocating library routine.
+ *
+ *   B * H * N must be at most FA_BWD_NOALLOC_MAX_ROWS (FA_ERR_TOO_LARGE
+ *   beyond, checked before any HIP call).
+ *
+ * All calls on one device share that device's array, whose contents persist
+ * from call to call (each call writes every D_i it reads before reading it).
+ * Calls that overlap in time on one device -- on different streams, or from
+ * different threads without ordering -- race on it and may return wrong
+ * gradients; serialise them (one stream, or events between streams).
+ */
+#define FA_BWD_NOALLOC_MAX_ROWS 4194304
+int fa_bwd_noalloc(const void *q, const void *k, const void *v, const void *o, const void *do_,
+                   const float *lse, void *dq, void *dk, void *dv,
+                   int B, int H, int N, int d, float scale, int causal, int dtype, void *stream);
 
 /*
  * fa_fwd_fa1_order -- the forward with the FlashAttention-1 loop order, kept

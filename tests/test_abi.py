@@ -14,7 +14,7 @@ from exact_attention_fa2_amd import build as fabuild
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
 
-OK, NULL, DIM, UNSUP, SCALE, ALIGN, LAUNCH, ALIAS, DEVICE = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, NULL, DIM, UNSUP, SCALE, ALIGN, LAUNCH, ALIAS, DEVICE, TOO_LARGE = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 A = 0x7F0000000000  # fake, 16-byte aligned device addresses (never touched)
 MB = 1 << 20
 
@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_header_declares_expected_entry_points():
     names = declared_functions()
-    for n in ("fa_fwd", "fa_fwd_strided", "fa_fwd_varlen", "fa_bwd", "fa_bwd_workspace_bytes",
+    for n in ("fa_fwd", "fa_fwd_strided", "fa_fwd_varlen", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_noalloc",
               "fa_fwd_fa1_order", "fa_fwd_fa1_workspace_bytes", "fa_strerror", "fa_version"):
         assert n in names
 
@@ -47,7 +47,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_strerror_and_version(L):
-    for code in (OK, NULL, DIM, UNSUP, SCALE, ALIGN, LAUNCH, ALIAS, DEVICE):
+    for code in (OK, NULL, DIM, UNSUP, SCALE, ALIGN, LAUNCH, ALIAS, DEVICE, TOO_LARGE):
         s = L.fa_strerror(code).decode()
         assert s and "unknown" not in s
     assert "unknown" in L.fa_strerror(12345).decode()
@@ -243,3 +243,27 @@ def test_python_wrappers_check_layout_before_any_gpu_call(L):
     # outputs of the wrappers are dense whatever the inputs' memory format
     x = torch.zeros(1, 2, 4, 64, dtype=torch.float16).to(memory_format=torch.channels_last)
     assert not x.is_contiguous() and torch.empty_like(x, memory_format=torch.contiguous_format).is_contiguous()
+
+
+def test_bwd_noalloc_argument_errors(L):
+    def call(**kw):
+        a = dict(q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, do=A + 256 * MB, lse=A + 320 * MB,
+                 dq=A + 384 * MB, dk=A + 448 * MB, dv=A + 512 * MB,
+                 B=1, H=2, N=64, d=64, scale=0.125, causal=0, dtype=1)
+        a.update(kw)
+        return L.fa_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                                a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"], a["dtype"], None)
+    assert fa.BWD_NOALLOC_MAX_ROWS == 4194304
+    assert "#define FA_BWD_NOALLOC_MAX_ROWS 4194304" in open(HEADER).read()
+    # B*H*N one past the static array is refused with the sizes, before any pointer
+    n = fa.BWD_NOALLOC_MAX_ROWS // 64 + 1
+    assert call(H=64, N=n, q=None) == TOO_LARGE
+    assert call(H=64, N=fa.BWD_NOALLOC_MAX_ROWS // 64, q=None) == NULL  # at the limit: size accepted
+    assert call(do=None) == NULL
+    assert call(dq=A + 384 * MB + 2) == ALIGN
+    assert call(dk=A) == ALIAS
+    assert call(dv=A + 448 * MB) == ALIAS
+    assert call(d=256) == UNSUP
+    assert call(scale=float("inf")) == SCALE
+    assert call(N=0, q=None) == OK
+    assert call() == DEVICE  # valid arguments, no GPU in this process
