@@ -22,9 +22,10 @@
 //    with ds_read_b64_tr_b16, the gfx950 LDS transpose read.
 //  * Softmax runs in the log2 domain: c = |scale|*log2(e), p = exp2(s*c - m).
 //    A negative scale is folded into Q by flipping its sign bits (exact).
-//  * The reference m of a row is its first tile's max. Later tiles skip the
-//    max entirely: their weights p = exp2(s*c - m) are formed with the
-//    standing m and only their partial sums are checked; a tile whose
+//  * The reference m of a row is its first tile's max (raised by 16 log2
+//    units for bf16, see ref_margin). Later tiles skip the max entirely:
+//    their weights p = exp2(s*c - m) are formed with the standing m and
+//    only their partial sums are checked; a tile whose
 //    partial sums reach partial_cap (so some weight could leave the 16-bit
 //    range) is redone with the true max and a rescale of the output
 //    accumulator. In the bf16 kernel for small grids the sum of the 16-bit
@@ -79,6 +80,17 @@ constexpr float partial_cap() {
   return DT == DT_BF16 ? 4294967296.0f : 32768.0f;
 }
 
+// A row's reference max is its first tile's max raised by this many log2
+// units. bf16 weights keep their relative precision far below 1 (8 exponent
+// bits), so the first tile's weights may start at 2^-16 and later tiles need
+// a score 16 + 32 units above the first tile's max before the range check
+// redoes a tile; large-logit rows then almost never redo. fp16 weights would
+// lose precision below 2^-14, so they keep the first tile's max.
+template <int DT>
+constexpr float ref_margin() {
+  return DT == DT_BF16 ? 16.0f : 0.0f;
+}
+
 // dword 3 of a raw buffer descriptor on gfx950 (32-bit data format, raw
 // addressing; loads past num_records return zero)
 constexpr int kBufferDword3 = 0x00020000;
@@ -92,6 +104,47 @@ struct FwdSmem {
   static constexpr int STAGE = KTILE + VTILE;
   static constexpr int BYTES = 2 * STAGE * 2;
 };
+
+// Workgroup -> (batch*head, query-block rank), XCD-aware: the order of
+// fa_fwd_kernel (which keeps it inline), as a function for the other
+// forward kernels. Workgroups are
+// dealt round-robin over the 8 XCDs and dispatched in order. Equal-length
+// sequences:
+//  * non-causal: each XCD takes a contiguous run of whole heads, whose blocks
+//    then share K/V in that XCD's L2;
+//  * causal: block rank major, head minor, so that the longest blocks of
+//    every head start first (a head-major order leaves long blocks of the
+//    last heads for the end), and with B*H a multiple of 8 every block of a
+//    head still lands on one XCD. With long rows (32 or more blocks a head)
+//    and B*H a multiple of 16, each XCD takes its heads in pairs, rank major
+//    within a pair: as fast, with two heads' K/V in flight per XCD instead of
+//    all of them (N=8192 x32 heads: 0.63x the fetched bytes).
+// Packed sequences of different lengths keep the plain order: a contiguous
+// run would hand the long sequences to a few XCDs, while the plain order
+// spreads every sequence's blocks over all eight (re-reads of K/V across XCDs
+// hit the shared Infinity Cache). Returns false for a padding workgroup.
+__device__ __forceinline__ bool fwd_block_of(const FwdArgs& a, int bid, int nblocks, bool causal, int& bh,
+                                             int& qi) {
+  if (causal && !a.cu_seqlens) {
+    const int nbh = a.B * a.H;
+    if ((nbh & 15) == 0 && a.nqb >= 32) {
+      const int x = bid & 7, j = bid >> 3;  // XCD, position in its order
+      const int grp = j / (2 * a.nqb), r = j - grp * 2 * a.nqb;
+      qi = r >> 1;
+      bh = x + 8 * (2 * grp + (r & 1));
+      return bh < nbh;
+    }
+    qi = bid / nbh;
+    bh = bid - qi * nbh;
+    return qi < a.nqb;
+  }
+  const int per = nblocks >> 3;
+  const int lid = a.cu_seqlens ? bid : (bid & 7) * per + (bid >> 3);
+  if (lid >= a.total) return false;
+  bh = lid / a.nqb;
+  qi = lid - bh * a.nqb;
+  return true;
+}
 
 // XOR swizzle of the 16-byte chunk slot of row r in an unpadded LDS tile
 // (rows of D halves). LDS has 64 banks; a 16-byte read is served 16 lanes at
@@ -248,7 +301,7 @@ __device__ __forceinline__ void tile_step_fwd(bool first, bool masked, const uin
     };
     // the first tile of a row sets its reference max (the accumulator is
     // still zero, so nothing needs rescaling)
-    if (first) m_run[j] = tile_max();
+    if (first) m_run[j] = tile_max() + ref_margin<DT>();
     probs(m_run[j] == -INFINITY ? 0.f : m_run[j]);
     const float pk = LS ? fmaxf(fmaxf(lf[0], lf[1]), fmaxf(lf[2], lf[3]))
                         : fmaxf(fmaxf(lp[0], lp[1]), fmaxf(lp[2], lp[3]));
