@@ -82,7 +82,11 @@ __global__ __launch_bounds__(NS * 64) void fa_fwd_split_kernel(const FwdArgs a) 
   float* Lg = a.lse + b * a.lse_sb + h * a.lse_sh + row0;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  // The wave index, visibly uniform: each wave's key range, buffer
+  // descriptors and LDS-DMA bases then sit in scalar registers, with no
+  // per-lane loop around each DMA (N=400 x4 heads fp16 8.5 -> 7.7 us,
+  // N=2048 x4 heads bf16 16.0 -> 14.0 us).
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
 
   // this wave's tiles: a contiguous run of ceil(ntiles / NS)
