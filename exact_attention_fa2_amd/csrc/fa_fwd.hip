@@ -42,6 +42,15 @@ int pick(FwdArgs a, hipStream_t st) {
   if constexpr (D == 64 || D == 128) {
     if (wg256 < 256) return launch_one<D, DT, CAUSAL, 4, 1, 64, k_prefetch<D, DT, 4>()>(a, st);
   }
+  if constexpr (D == 64) {
+    // maps of at most 128 rows: 2 heads (4 up to 64 rows) per workgroup, all
+    // of their K and V loaded at once (B=64 x16 heads N=64 fp16: 10.4 vs
+    // 13.3 us; B=64 x8 heads N=100 bf16: 10.8 vs 12.7 us). Longer maps keep
+    // the kernels below: one head per workgroup with its whole K/V in LDS
+    // lost at N=400 x128 heads (16.5 vs 14.6 us bf16, 16.1 vs 14.4 us fp16).
+    if (a.cu_seqlens == nullptr && a.N <= 128)
+      return a.N <= 64 ? launch_resident<D, DT, CAUSAL, 4>(a, st) : launch_resident<D, DT, CAUSAL, 2>(a, st);
+  }
   if constexpr (D == 64 && DT == DT_BF16 && !CAUSAL) {
     // at most two 32-row units of work per SIMD (1024 SIMDs): the weight
     // sums by MFMA (N=400 x128 heads: 14.7-15.4 vs 15.0-15.8 us; with the

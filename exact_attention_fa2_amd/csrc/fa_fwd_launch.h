@@ -8,6 +8,7 @@
 
 #include "fa.h"
 #include "fa_fwd_kernel.h"
+#include "fa_fwd_resident.h"
 #include "fa_fwd_split.h"
 
 namespace fa {
@@ -60,6 +61,24 @@ int launch_one(FwdArgs a, hipStream_t st) {
   const int grid = (a.total + 7) / 8 * 8;  // a multiple of the 8 XCDs
   (void)hipGetLastError();
   hipLaunchKernelGGL((fa_fwd_kernel<D, DT, CAUSAL, NW, QB, BC, PF, LS>), dim3(grid), dim3(NW * 64), 0, st, a);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+// The head-packed kernel for equal-length maps of at most 32 * 8 / HP rows:
+// HP heads per 8-wave workgroup.
+template <int D, int DT, bool CAUSAL, int HP>
+int launch_resident(FwdArgs a, hipStream_t st) {
+  if (a.N > 32 * (8 / HP) || a.cu_seqlens) return FA_ERR_DIM;
+  const int64_t groups = ((int64_t)a.B * a.H + HP - 1) / HP;
+  if (groups > (INT64_C(1) << 30)) return FA_ERR_DIM;
+  const int64_t lds = resident_lds_bytes<D, HP>(a.N);
+  static const bool attr = hipFuncSetAttribute((const void*)fa_fwd_resident_kernel<D, DT, CAUSAL, HP>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)resident_lds_bytes<D, HP>(32 * (8 / HP))) == hipSuccess;
+  (void)attr;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL((fa_fwd_resident_kernel<D, DT, CAUSAL, HP>), dim3((unsigned)groups), dim3(512), (unsigned)lds,
+                     st, a);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -255,6 +255,19 @@ def test_bf16_small_grid_mfma_weight_sums(B, H, N, sigma):
     run_case(B, H, N, 64, "bf16", False, 60 + B, None, sigma, 1.0, rows)
 
 
+@pytest.mark.parametrize("B,H,N,dtype,causal,sigma", [
+    (3, 181, 100, "f16", False, 1.0), (2, 150, 128, "bf16", True, 3.0), (4, 70, 65, "bf16", False, 2.0),
+    (5, 111, 64, "bf16", True, 3.0), (7, 80, 17, "f16", False, 1.0), (1, 601, 1, "bf16", False, 1.0),
+    (3, 95, 33, "f16", True, 1.0), (9, 57, 32, "bf16", False, 2.5)])
+def test_head_packed_short_maps(B, H, N, dtype, causal, sigma):
+    # d=64 maps of at most 128 rows on grids past the key-split (more than 512
+    # units of 32 rows) and 4-wave (256+ heads) limits: 2 heads per workgroup,
+    # 4 up to 64 rows; head counts that leave the last workgroup partly empty
+    units = B * H * ((N + 31) // 32)
+    assert units > 512 and B * H >= 256, "shape must reach the head-packed kernel"
+    run_case(B, H, N, 64, dtype, causal, 90 + N, None, sigma, 1.0)
+
+
 def test_deterministic():
     q, k, v = (t.to(DEV) for t in inputs.make_qkv(2, 4, 1000, 64, "f16", 51))
     o1, l1 = fa.attention(q, k, v, causal=True)
