@@ -105,47 +105,6 @@ struct FwdSmem {
   static constexpr int BYTES = 2 * STAGE * 2;
 };
 
-// Workgroup -> (batch*head, query-block rank), XCD-aware: the order of
-// fa_fwd_kernel (which keeps it inline), as a function for the other
-// forward kernels. Workgroups are
-// dealt round-robin over the 8 XCDs and dispatched in order. Equal-length
-// sequences:
-//  * non-causal: each XCD takes a contiguous run of whole heads, whose blocks
-//    then share K/V in that XCD's L2;
-//  * causal: block rank major, head minor, so that the longest blocks of
-//    every head start first (a head-major order leaves long blocks of the
-//    last heads for the end), and with B*H a multiple of 8 every block of a
-//    head still lands on one XCD. With long rows (32 or more blocks a head)
-//    and B*H a multiple of 16, each XCD takes its heads in pairs, rank major
-//    within a pair: as fast, with two heads' K/V in flight per XCD instead of
-//    all of them (N=8192 x32 heads: 0.63x the fetched bytes).
-// Packed sequences of different lengths keep the plain order: a contiguous
-// run would hand the long sequences to a few XCDs, while the plain order
-// spreads every sequence's blocks over all eight (re-reads of K/V across XCDs
-// hit the shared Infinity Cache). Returns false for a padding workgroup.
-__device__ __forceinline__ bool fwd_block_of(const FwdArgs& a, int bid, int nblocks, bool causal, int& bh,
-                                             int& qi) {
-  if (causal && !a.cu_seqlens) {
-    const int nbh = a.B * a.H;
-    if ((nbh & 15) == 0 && a.nqb >= 32) {
-      const int x = bid & 7, j = bid >> 3;  // XCD, position in its order
-      const int grp = j / (2 * a.nqb), r = j - grp * 2 * a.nqb;
-      qi = r >> 1;
-      bh = x + 8 * (2 * grp + (r & 1));
-      return bh < nbh;
-    }
-    qi = bid / nbh;
-    bh = bid - qi * nbh;
-    return qi < a.nqb;
-  }
-  const int per = nblocks >> 3;
-  const int lid = a.cu_seqlens ? bid : (bid & 7) * per + (bid >> 3);
-  if (lid >= a.total) return false;
-  bh = lid / a.nqb;
-  qi = lid - bh * a.nqb;
-  return true;
-}
-
 // XOR swizzle of the 16-byte chunk slot of row r in an unpadded LDS tile
 // (rows of D halves). LDS has 64 banks; a 16-byte read is served 16 lanes at
 // a time and an 8-byte transposing read 32 lanes at a time, so the slot must
