@@ -35,6 +35,19 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
                                                    __builtin_bit_cast(b16x8, b), c, 0, 0, 0);
 }
 
+// D(16x16, fp32) += A(16x32) * B(32x16); each lane holds 8 16-bit values of A
+// (row lane%16, k = 8*(lane/16)..+7) and of B (column lane%16, same k), and
+// 4 fp32 of D (row 4*(lane/16) + r, column lane%16).
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (DT == DT_F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h16x8, a),
+                                                  __builtin_bit_cast(h16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b16x8, a),
+                                                   __builtin_bit_cast(b16x8, b), c, 0, 0, 0);
+}
+
 // Two fp32 -> one dword of two 16-bit values (round to nearest even); `lo`
 // lands in the low half.
 template <int DT>

@@ -51,6 +51,16 @@ int pick(FwdArgs a, hipStream_t st) {
     if (a.cu_seqlens == nullptr && a.N <= 128)
       return a.N <= 64 ? launch_resident<D, DT, CAUSAL, 4>(a, st) : launch_resident<D, DT, CAUSAL, 2>(a, st);
   }
+  if constexpr (D == 64 && CAUSAL) {
+    // causal, at most 2048 units of 32 rows: 16-row units in 4-wave
+    // workgroups (N=400 x128 heads bf16: 11.3 vs 14.9 us; N=256 x256 heads
+    // fp16: 10.4 vs 12.7 us; N=1000 x64 heads fp16: 20.0 vs 25.2 us). With
+    // more units they lose (N=400 x256 heads fp16: 19.3 vs 18.3 us); without
+    // the mask the units are equal and the 32-row kernels are as fast or
+    // faster (N=400 x128 heads: 14.8 vs 15.0 us; x256 fp16: 26.3 vs 24.8).
+    if (a.cu_seqlens == nullptr && (int64_t)a.B * a.H * ((a.N + 31) / 32) <= 2048)
+      return launch_fwd16<D, DT, CAUSAL, 4>(a, st);
+  }
   if constexpr (D == 64 && DT == DT_BF16 && !CAUSAL) {
     // at most two 32-row units of work per SIMD (1024 SIMDs): the weight
     // sums by MFMA (N=400 x128 heads: 14.7-15.4 vs 15.0-15.8 us; with the

@@ -8,6 +8,7 @@
 
 #include "fa.h"
 #include "fa_fwd_kernel.h"
+#include "fa_fwd16.h"
 #include "fa_fwd_resident.h"
 #include "fa_fwd_split.h"
 
@@ -79,6 +80,21 @@ int launch_resident(FwdArgs a, hipStream_t st) {
   (void)hipGetLastError();
   hipLaunchKernelGGL((fa_fwd_resident_kernel<D, DT, CAUSAL, HP>), dim3((unsigned)groups), dim3(512), (unsigned)lds,
                      st, a);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+// The 16-row-unit kernel (causal, equal lengths): units of 16 query rows,
+// at most NW a block, blocks by rank across heads.
+template <int D, int DT, bool CAUSAL, int NW>
+int launch_fwd16(FwdArgs a, hipStream_t st) {
+  if (a.cu_seqlens || !CAUSAL) return FA_ERR_DIM;
+  a.units = (a.N + 15) / 16;
+  a.nqb = (a.units + NW - 1) / NW;
+  const int64_t total = (int64_t)a.B * a.H * a.nqb;
+  if (total > (INT64_C(1) << 30)) return FA_ERR_DIM;
+  a.total = (int)total;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL((fa_fwd16_kernel<D, DT, CAUSAL, NW>), dim3(a.total), dim3(NW * 64), 0, st, a);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -268,6 +268,29 @@ def test_head_packed_short_maps(B, H, N, dtype, causal, sigma):
     run_case(B, H, N, 64, dtype, causal, 90 + N, None, sigma, 1.0)
 
 
+@pytest.mark.parametrize("B,H,N,dtype,sigma", [
+    (8, 16, 400, "bf16", 3.0), (32, 8, 256, "f16", 1.0), (2, 64, 333, "f16", 1.0), (4, 32, 500, "bf16", 2.5),
+    (8, 8, 1000, "f16", 1.0), (4, 16, 1000, "bf16", 3.0), (1, 300, 129, "bf16", 1.0), (2, 70, 401, "f16", 2.0)])
+def test_causal_16_row_units(B, H, N, dtype, sigma):
+    # causal d=64 grids of 513..2048 units of 32 rows with 256+ workgroups of
+    # 256 rows: 16-row units (16x16x32 MFMAs) in 4-wave workgroups; ragged
+    # ends at 1, 15, 16 and 17 rows past a 64-key tile
+    units = B * H * ((N + 31) // 32)
+    assert 512 < units <= 2048 and B * H * ((N + 255) // 256) >= 256, "shape must reach the 16-row kernel"
+    rows = P.sample_rows(B, H, N, 400, N) if B * H * N * N > 40_000_000 else None
+    eo, el = run_case(B, H, N, 64, dtype, True, 110 + N, None, sigma, 1.0, rows)
+    if rows is not None:
+        # one whole head too, from a launch of the same grid
+        q, k, v = inputs.make_qkv(B, H, N, 64, dtype, 110 + N, sigma, 1.0)
+        o, lse = fa.attention(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, scale=64 ** -0.5)
+        torch.cuda.synchronize()
+        b, h = B - 1, H // 2
+        qd, kd, vd = (P.decode(x[b:b + 1, h:h + 1], dtype) for x in (q, k, v))
+        ro, rl = oracle.attention_fwd(qd, kd, vd, 64 ** -0.5, True)
+        P.gate_o(P.to64(o)[b:b + 1, h:h + 1], ro, dtype)
+        P.gate_lse(P.to64(lse)[b:b + 1, h:h + 1], rl)
+
+
 def test_deterministic():
     q, k, v = (t.to(DEV) for t in inputs.make_qkv(2, 4, 1000, 64, "f16", 51))
     o1, l1 = fa.attention(q, k, v, causal=True)
