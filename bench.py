@@ -52,7 +52,7 @@ def log(*a):
 
 # the files the forward kernels are built from (code, dispatch, build options)
 FWD_SOURCES = ("csrc/fa_device.h", "csrc/fa_fwd_kernel.h", "csrc/fa_fwd.hip", "csrc/fa_fwd_split.h",
-               "csrc/fa_fwd_resident.h", "csrc/fa_fwd_launch.h", "csrc/fa_fwd_small.hip", "build.py")
+               "csrc/fa_fwd_resident.h", "csrc/fa_fwd16.h", "csrc/fa_fwd_launch.h", "csrc/fa_fwd_small.hip", "build.py")
 
 
 def kernel_source_hash() -> str:
