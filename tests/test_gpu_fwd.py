@@ -291,6 +291,31 @@ def test_causal_16_row_units(B, H, N, dtype, sigma):
         P.gate_lse(P.to64(lse)[b:b + 1, h:h + 1], rl)
 
 
+@pytest.mark.parametrize("B,H,N,dtype,causal", [
+    (1, 256, 128, "bf16", False),   # head-packed, 2 heads a workgroup, at its 128-row limit
+    (1, 256, 129, "f16", False),    # one row past it: the 8-wave main kernel
+    (1, 256, 129, "bf16", False),   # ... or, bf16, the kernel with MFMA weight sums
+    (1, 257, 64, "f16", True),      # head-packed, 4 heads a workgroup, 513 units of 32 rows
+    (1, 256, 64, "bf16", False),    # 512 units: still the key-split kernel
+    (1, 157, 400, "bf16", True),    # causal, 2041 units: 16-row kernel
+    (1, 158, 400, "f16", True),     # causal, 2054 units: the 8-wave main kernel
+    (1, 255, 256, "f16", False),    # 255 workgroups of 256 rows: the 4-wave main kernel
+    (1, 128, 512, "bf16", True)])   # causal, 2048 units, 256 workgroups of 256 rows: 16-row kernel
+def test_dispatch_boundaries(B, H, N, dtype, causal):
+    # shapes on either side of each d=64 dispatch bound, against the oracle
+    # on 400 sampled rows (every head) plus one whole head
+    rows = P.sample_rows(B, H, N, 400, B * H + N)
+    run_case(B, H, N, 64, dtype, causal, 130 + H, None, 2.0, 1.0, rows)
+    q, k, v = inputs.make_qkv(B, H, N, 64, dtype, 130 + H, 2.0, 1.0)
+    o, lse = fa.attention(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, scale=64 ** -0.5)
+    torch.cuda.synchronize()
+    h = H - 1
+    qd, kd, vd = (P.decode(x[:, h:h + 1], dtype) for x in (q, k, v))
+    ro, rl = oracle.attention_fwd(qd, kd, vd, 64 ** -0.5, causal)
+    P.gate_o(P.to64(o)[:, h:h + 1], ro, dtype)
+    P.gate_lse(P.to64(lse)[:, h:h + 1], rl)
+
+
 def test_deterministic():
     q, k, v = (t.to(DEV) for t in inputs.make_qkv(2, 4, 1000, 64, "f16", 51))
     o1, l1 = fa.attention(q, k, v, causal=True)
