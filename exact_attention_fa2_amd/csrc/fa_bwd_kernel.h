@@ -137,7 +137,10 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dkdv_kernel(const BwdArgs a) {
   const float* Dg = a.dvec + (int64_t)bh * a.N;
   const int N = a.N;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // the wave index read from the first lane, so that what derives from it
+  // (tile ranges, buffer descriptors, LDS-DMA bases) is scalar: no per-lane
+  // loop around loads (N=8192 causal d=128: 1875 -> 1785 us per backward)
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int kw0 = kblk * 128 + w * 32;  // first key of this wave
   const int krow = kw0 + l32;
@@ -351,7 +354,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv_wide_kernel(const B
   const float* Dg = a.dvec + (int64_t)bh * a.N;
   const int N = a.N;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int kw0 = kblk * KW + w * 32;  // first key of this wave
   const int krow = kw0 + l32;
@@ -556,7 +559,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_bwd_dq_kernel(con
   const uint16_t* Gg = a.dout + off;
   const int N = a.N;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int qw0 = qblk * BR + w * 32;
   const int qrow = qw0 + l32;
@@ -746,7 +749,7 @@ __global__ __launch_bounds__(NW * 64) void fa_bwd_dq_staged_kernel(const BwdArgs
   const uint16_t* Gg = a.dout + off;
   const int N = a.N;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int qw0 = qblk * BR + w * 32;
   const int qrow = qw0 + l32;
