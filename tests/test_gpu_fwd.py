@@ -410,6 +410,32 @@ def test_bnhd_and_packed_layouts(causal):
     assert torch.equal(o2.cpu(), o.cpu()) and torch.equal(lse2.cpu(), lse.cpu())
 
 
+@pytest.mark.parametrize("B,N,H,dtype,causal", [
+    (4, 100, 70, "bf16", False),   # head-packed kernel, 2 heads a workgroup
+    (3, 60, 90, "f16", True),      # head-packed kernel, 4 heads a workgroup
+    (2, 400, 70, "f16", True),     # causal 16-row kernel
+    (1, 640, 300, "bf16", False)])  # the 8-wave main kernel
+def test_strided_layouts_on_short_map_kernels(B, N, H, dtype, causal):
+    # the short-map kernels address Q, K, V and O through the row, head and
+    # batch strides: [B, N, H, d] views and packed QKV against the oracle
+    say(f"[fa_fwd_strided] short maps B{B} N{N} H{H} {dtype} causal={causal}")
+    d = 64
+    q, k, v = inputs.make_qkv(B, N, H, d, dtype, 150 + N)  # drawn directly in [B, N, H, d]
+    o, lse = fa.attention_bnhd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal)
+    torch.cuda.synchronize()
+    perm = lambda t: P.decode(t, dtype).transpose(0, 2, 1, 3)
+    qd, kd, vd = perm(q), perm(k), perm(v)
+    rows = P.sample_rows(B, H, N, 400, N)
+    ro, rl = oracle.attention_fwd_rows(qd, kd, vd, d ** -0.5, causal, rows)
+    og, lg = P.to64(o).transpose(0, 2, 1, 3), P.to64(lse)
+    P.gate_o(og[rows[:, 0], rows[:, 1], rows[:, 2]], ro, dtype)
+    P.gate_lse(lg[rows[:, 0], rows[:, 1], rows[:, 2]], rl)
+    qkv = torch.stack([q, k, v], dim=2).contiguous()  # [B, N, 3, H, d]
+    o2, lse2 = fa.attention_qkvpacked(qkv.to(DEV), causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.cpu(), o.cpu()) and torch.equal(lse2.cpu(), lse.cpu())
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_packed_qkv_pages_shape(d):
     # an 80x80 map with C = 256 channels split into heads of d
