@@ -316,6 +316,30 @@ def test_dispatch_boundaries(B, H, N, dtype, causal):
     P.gate_lse(P.to64(lse)[:, h:h + 1], rl)
 
 
+def _random_shapes(n, seed=2026):
+    # seeded shapes over the dispatch regimes: few or many heads, short or
+    # long rows, ragged lengths, both head dims of the short-map kernels
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        d = int(rng.choice([64, 128]))
+        N = int(rng.choice([int(rng.integers(1, 130)), int(rng.integers(130, 1100))]))
+        BH = int(rng.choice([int(rng.integers(1, 40)), int(rng.integers(200, 700))]))
+        if BH * N * d > 40_000_000:
+            continue
+        B = int(rng.integers(1, 4))
+        H = max(1, BH // B)
+        out.append((B, H, N, d, str(rng.choice(["f16", "bf16"])), bool(rng.integers(0, 2)),
+                    float(rng.choice([1.0, 2.0, 3.0]))))
+    return out
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype,causal,sigma", _random_shapes(24))
+def test_random_shapes(B, H, N, d, dtype, causal, sigma):
+    rows = P.sample_rows(B, H, N, 300, B * H + N) if B * H * N * N > 4_000_000 else None
+    run_case(B, H, N, d, dtype, causal, 170 + N, None, sigma, 1.0, rows)
+
+
 def test_deterministic():
     q, k, v = (t.to(DEV) for t in inputs.make_qkv(2, 4, 1000, 64, "f16", 51))
     o1, l1 = fa.attention(q, k, v, causal=True)
