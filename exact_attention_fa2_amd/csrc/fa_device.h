@@ -86,7 +86,11 @@ __device__ __forceinline__ float to_f32(uint16_t x) {
 // addressed by lanes i/4, i/4 + 4, i/4 + 8 and i/4 + 12 of its group, in that
 // order. Pointing lane s at row r0 + s/4, column c0 + 4*(s%4) of a row-major
 // 16-bit matrix therefore hands lane i the column c0 + i of rows r0..r0+3.
-__device__ __forceinline__ u32x2 lds_read_tr4(const uint16_t* p) {
+// The __restrict__ gives the read alias-scope information. Without it the
+// compiler cannot tell that the read does not touch LDS being filled by an
+// LDS-DMA load in flight, and makes it wait for every such load. The kernels
+// order DMA-filled tiles and their reads with their own waits and barriers.
+__device__ __forceinline__ u32x2 lds_read_tr4(const uint16_t* __restrict__ p) {
   typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
   i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
   return __builtin_bit_cast(u32x2, r);
