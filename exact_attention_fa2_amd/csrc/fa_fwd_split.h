@@ -124,16 +124,13 @@ __global__ __launch_bounds__(NS * 64) void fa_fwd_split_kernel(const FwdArgs a) 
     }
   };
 
-  // Q fragments (rows past the end are zero; a negative scale flips signs)
+  // Q fragments (rows past the end are zero; a negative scale flips signs).
+  // They are loaded raw and converted once the first tile's DMA has been
+  // issued, so that the wait for Q does not hold back that DMA.
   u32x4 qf[1][KK];
-  {
-    const int r = qw0 + l32;
+  const int qr = qw0 + l32;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const u32x4 x = *(const u32x4*)(Qg + min(r, Nb - 1) * a.q_sr + 16 * kk + 8 * hh);
-      qf[0][kk] = (r < Nb ? x : u32x4{0u, 0u, 0u, 0u}) ^ a.qsign;
-    }
-  }
+  for (int kk = 0; kk < KK; ++kk) qf[0][kk] = *(const u32x4*)(Qg + min(qr, Nb - 1) * a.q_sr + 16 * kk + 8 * hh);
 
   f32x16 oacc[1][DB];
 #pragma unroll
@@ -143,7 +140,10 @@ __global__ __launch_bounds__(NS * 64) void fa_fwd_split_kernel(const FwdArgs a) 
   float m_run[1] = {-INFINITY}, l_run[2][1] = {{0.f}, {0.f}};
 
   if (t_begin < t_end) {
+    __builtin_amdgcn_sched_barrier(0);  // the Q loads stay ahead of the DMA
     dma(t_begin, 0);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qf[0][kk] = (qr < Nb ? qf[0][kk] : u32x4{0u, 0u, 0u, 0u}) ^ a.qsign;
     for (int t = t_begin; t < t_end; ++t) {
       const int buf = NB == 2 ? (t - t_begin) & 1 : 0;
       if (NB == 2 && t + 1 < t_end) {
