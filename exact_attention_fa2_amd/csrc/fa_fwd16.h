@@ -149,7 +149,9 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd16_kernel(const FwdArgs a) {
   constexpr int KK = D / 32, DB = D / 16;
   constexpr int CH = BC * D / 8 / NT;  // 16-byte chunks per thread per tensor per tile
   static_assert(BC * D / 8 % NT == 0, "tile must split evenly over threads");
-  using SM = FwdSmem<D, BC>;
+  // (V rows of D+16 halves: the 16-row step reads 8 consecutive rows 32 lanes
+  // at a time, 8 banks each, which a stride of 40 or 72 banks keeps apart)
+  using SM = FwdSmem<D, BC, D + 16>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SM::STAGE];
 
   // workgroup -> (batch*head, query block): blocks run by rank across heads,

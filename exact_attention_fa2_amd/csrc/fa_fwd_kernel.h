@@ -95,10 +95,23 @@ constexpr float ref_margin() {
 // addressing; loads past num_records return zero)
 constexpr int kBufferDword3 = 0x00020000;
 
-template <int D, int BC>
+// Padded V row (halves) of the 32-row tile step. Its transposing reads are
+// served 32 lanes at a time over 64 banks of 4 bytes: 4 consecutive rows at
+// 8-byte steps across 64 bytes of columns, so each row covers 16 banks, and
+// the 4 rows are conflict-free when the row stride is 16 or 48 banks (mod 64),
+// i.e. VSTR = 32 or 96 halves (mod 128). d=64 and 96: 96; d=128 and 256: D+32.
+template <int D>
+constexpr int fwd_vstr() {
+  return D <= 96 ? 96 : D + 32;
+}
+static_assert(fwd_vstr<64>() % 128 == 96 && fwd_vstr<96>() % 128 == 96 && fwd_vstr<128>() % 128 == 32 &&
+                  fwd_vstr<256>() % 128 == 32,
+              "V rows at 16 or 48 banks");
+
+template <int D, int BC, int VS = fwd_vstr<D>()>
 struct FwdSmem {
-  static constexpr int KSTR = D + 8;   // padded K row (halves): conflict-free 16-byte reads
-  static constexpr int VSTR = D + 16;  // padded V row (halves): conflict-free transpose reads
+  static constexpr int KSTR = D + 8;  // padded K row (halves): conflict-free 16-byte reads
+  static constexpr int VSTR = VS;     // padded V row (halves)
   static constexpr int KTILE = BC * KSTR;
   static constexpr int VTILE = BC * VSTR;
   static constexpr int STAGE = KTILE + VTILE;
