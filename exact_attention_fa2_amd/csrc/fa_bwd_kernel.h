@@ -245,28 +245,35 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dkdv_kernel(const BwdArgs a) {
           dp = mfma32x32x16<DT>(ga, vf[kk], dp);
         }
       }
-      const bool diag = CAUSAL && qr0 < kw0 + 31;
+      // P and dS = P dP, packed; the causal mask of a diagonal block is a
+      // second copy of the loop under a uniform branch (a test inside the one
+      // loop became selects executed on every block)
       u32x4 pp[2], sp[2];
+      auto weights = [&](bool mask) __attribute__((always_inline)) {
+        // register r holds query qr0 + 8*(r/4) + 4*hh + r%4
+        const int lim = krow - (qr0 + 4 * hh);
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
+        for (int c2 = 0; c2 < 2; ++c2) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float pv[2], sv[2];
+          for (int e = 0; e < 4; ++e) {
+            float pv[2], sv[2];
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int r = 8 * c2 + 2 * e + u;
-            float p = fast_exp2(s[r] * a.c);
-            if (CAUSAL && diag) {
-              const int qrow = qr0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-              if (krow > qrow) p = 0.f;
+            for (int u = 0; u < 2; ++u) {
+              const int r = 8 * c2 + 2 * e + u;
+              float p = fast_exp2(s[r] * a.c);
+              if (mask && 8 * (r >> 2) + (r & 3) < lim) p = 0.f;
+              pv[u] = p;
+              if constexpr (WANT_DK) sv[u] = p * dp[r];
             }
-            pv[u] = p;
-            if constexpr (WANT_DK) sv[u] = p * dp[r];
+            if constexpr (WANT_DV) pp[c2][e] = pack2<DT>(pv[0], pv[1]);
+            if constexpr (WANT_DK) sp[c2][e] = pack2<DT>(sv[0], sv[1]);
           }
-          if constexpr (WANT_DV) pp[c2][e] = pack2<DT>(pv[0], pv[1]);
-          if constexpr (WANT_DK) sp[c2][e] = pack2<DT>(sv[0], sv[1]);
         }
-      }
+      };
+      if (CAUSAL && qr0 < kw0 + 31)
+        weights(true);
+      else
+        weights(false);
       // dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS ; k-slot 8*hh + 4*rd + e of chunk c2 is
       // query 16*c2 + 8*rd + 4*hh + e of this block
 #pragma unroll
@@ -471,28 +478,35 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv_wide_kernel(const B
       // phase boundaries for the scheduler: LDS reads hoisted across them
       // would hold registers through the exponentials (48 spilled)
       __builtin_amdgcn_sched_barrier(0);
-      const bool diag = CAUSAL && qr0 < kw0 + 31;
+      // P and dS = P dP, packed; the causal mask of a diagonal block is a
+      // second copy of the loop under a uniform branch (a test inside the one
+      // loop became selects executed on every block)
       u32x4 pp[2], sp[2];
+      auto weights = [&](bool mask) __attribute__((always_inline)) {
+        // register r holds query qr0 + 8*(r/4) + 4*hh + r%4
+        const int lim = krow - (qr0 + 4 * hh);
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
+        for (int c2 = 0; c2 < 2; ++c2) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float pv[2], sv[2];
+          for (int e = 0; e < 4; ++e) {
+            float pv[2], sv[2];
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int r = 8 * c2 + 2 * e + u;
-            float p = fast_exp2(s[r] * a.c);
-            if (CAUSAL && diag) {
-              const int qrow = qr0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-              if (krow > qrow) p = 0.f;
+            for (int u = 0; u < 2; ++u) {
+              const int r = 8 * c2 + 2 * e + u;
+              float p = fast_exp2(s[r] * a.c);
+              if (mask && 8 * (r >> 2) + (r & 3) < lim) p = 0.f;
+              pv[u] = p;
+              sv[u] = p * dp[r];
             }
-            pv[u] = p;
-            sv[u] = p * dp[r];
+            pp[c2][e] = pack2<DT>(pv[0], pv[1]);
+            sp[c2][e] = pack2<DT>(sv[0], sv[1]);
           }
-          pp[c2][e] = pack2<DT>(pv[0], pv[1]);
-          sp[c2][e] = pack2<DT>(sv[0], sv[1]);
         }
-      }
+      };
+      if (CAUSAL && qr0 < kw0 + 31)
+        weights(true);
+      else
+        weights(false);
       __builtin_amdgcn_sched_barrier(0);
       // dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS ; k-slot 8*hh + 4*rd + e of chunk c2 is
       // query 16*c2 + 8*rd + 4*hh + e of this block
@@ -679,7 +693,24 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_bwd_dq_kernel(con
     // phase boundaries for the scheduler (LDS reads hoisted across them
     // would hold registers through the exponentials)
     __builtin_amdgcn_sched_barrier(0);
+    // P in place of S; the mask runs as a loop of its own under a uniform
+    // branch (inside the loop above the compiler turned it into selects
+    // executed on every tile: 95 of the tile's 252 VALU instructions at d=64)
     const bool masked = key0 + BC > N || (CAUSAL && key0 + BC - 1 > qw0);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], a.c, -lq));
+    if (masked) {
+      // register r of block kb holds key key0 + 32*kb + 8*(r/4) + 4*hh + r%4
+      int lim = N - 1 - (key0 + 4 * hh);
+      if constexpr (CAUSAL) lim = min(lim, qrow - (key0 + 4 * hh));
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = 0.f;
+    }
     u32x4 sf[BC / 16];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -688,18 +719,8 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_bwd_dq_kernel(con
         u32x4 x;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float v2[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int r = 8 * c2 + 2 * e + u;
-            float p = fast_exp2(__builtin_fmaf(s[kb][r], a.c, -lq));
-            if (masked) {
-              const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-              if (key >= N || (CAUSAL && key > qrow)) p = 0.f;
-            }
-            v2[u] = p * dp[kb][r];
-          }
-          x[e] = pack2<DT>(v2[0], v2[1]);
+          const int r = 8 * c2 + 2 * e;
+          x[e] = pack2<DT>(s[kb][r] * dp[kb][r], s[kb][r + 1] * dp[kb][r + 1]);
         }
         sf[2 * kb + c2] = x;
       }
@@ -840,7 +861,23 @@ __global__ __launch_bounds__(NW * 64) void fa_bwd_dq_staged_kernel(const BwdArgs
         s[kb] = mfma32x32x16<DT>(ka, qf[kk], s[kb]);
         dp[kb] = mfma32x32x16<DT>(va, gf[kk], dp[kb]);
       }
+    // P in place of S; the mask as a loop of its own under a uniform branch
+    // (folded into the exponentials' loop it became selects on every tile)
     const bool masked = key0 + BC > N || (CAUSAL && key0 + BC - 1 > qw0);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], a.c, -lq));
+    if (masked) {
+      // register r of block kb holds key key0 + 32*kb + 8*(r/4) + 4*hh + r%4
+      int lim = N - 1 - (key0 + 4 * hh);
+      if constexpr (CAUSAL) lim = min(lim, qrow - (key0 + 4 * hh));
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = 0.f;
+    }
     u32x4 sf[BC / 16];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -849,18 +886,8 @@ __global__ __launch_bounds__(NW * 64) void fa_bwd_dq_staged_kernel(const BwdArgs
         u32x4 x;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float v2[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int r = 8 * c2 + 2 * e + u;
-            float p = fast_exp2(__builtin_fmaf(s[kb][r], a.c, -lq));
-            if (masked) {
-              const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-              if (key >= N || (CAUSAL && key > qrow)) p = 0.f;
-            }
-            v2[u] = p * (dp[kb][r] - dq_row);
-          }
-          x[e] = pack2<DT>(v2[0], v2[1]);
+          const int r = 8 * c2 + 2 * e;
+          x[e] = pack2<DT>(s[kb][r] * (dp[kb][r] - dq_row), s[kb][r + 1] * (dp[kb][r + 1] - dq_row));
         }
         sf[2 * kb + c2] = x;
       }
