@@ -463,10 +463,14 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv_wide_kernel(const B
     const uint16_t* sg = sq + TILE;
     const float* sl = (const float*)(sg + TILE);
     const int q0 = t * BQ;
-#pragma unroll 1
-    for (int qb = 0; qb < BQ / 32; ++qb) {
+    // one 32-query block; the non-causal loop over blocks is unrolled, so that
+    // the second block's LDS addresses are the first block's plus an immediate
+    // offset (the swizzle depends only on the low 4 bits of a row) instead of
+    // 31 address instructions a block; the causal one, with its masked copy of
+    // the weights, would spill unrolled
+    auto qblock = [&](int qb) __attribute__((always_inline)) {
       const int qr0 = q0 + 32 * qb;
-      if (CAUSAL && qr0 + 31 < kw0) continue;  // every query precedes every key
+      if (CAUSAL && qr0 + 31 < kw0) return;  // every query precedes every key
       f32x16 s = load_rowvals(sl + 32 * qb, hh), dp = load_rowvals(sl + BQ + 32 * qb, hh);
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
@@ -524,6 +528,13 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv_wide_kernel(const B
           dk[db] = mfma32x32x16<DT>(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, sp[c2], dk[db]);
         }
       }
+    };
+    if constexpr (CAUSAL) {
+#pragma unroll 1
+      for (int qb = 0; qb < BQ / 32; ++qb) qblock(qb);
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < BQ / 32; ++qb) qblock(qb);
     }
     if (t + 1 < nt) stash_rows(buf ^ 1);
   }
