@@ -56,7 +56,7 @@ def run(B, H, N, d, dtype, causal, seed, sigma_qk=1.0, scale=None):
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N,d,dtype", [(1, 64, "f16"), (64, 64, "bf16"), (200, 64, "f16"), (400, 64, "bf16"),
                                        (129, 128, "f16"), (300, 128, "bf16"), (97, 96, "f16"), (1000, 64, "f16"),
-                                       (700, 128, "bf16")])
+                                       (700, 128, "bf16"), (333, 96, "bf16"), (1030, 96, "f16")])
 def test_bwd_matches_oracle(N, d, dtype, causal):
     run(2, 2, N, d, dtype, causal, seed=N + d)
 
