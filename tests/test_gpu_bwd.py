@@ -109,3 +109,24 @@ def test_bwd_workload_sampled_heads(name):
         for gname, g, r in zip(("dq", "dk", "dv"), grads, refs):
             rel[gname] = gate_grad(g[b:b + 1, h:h + 1], r, w.dtype, f"{gname} head ({b},{h})", floor)
         print(f"  head ({b},{h}) rel errors", {k2: f"{v2:.2e}" for k2, v2 in rel.items()}, flush=True)
+
+
+def _random_bwd_shapes(n, seed=2027):
+    # seeded shapes across the backward's regimes: every head dim it takes,
+    # one or several key/query blocks, ragged lengths, both causal modes,
+    # larger logits and scales of either sign
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        d = int(rng.choice([64, 96, 128]))
+        N = int(rng.integers(1, 140)) if rng.random() < 0.3 else int(rng.integers(140, 1100))
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        sc = float(rng.choice([d ** -0.5, -(d ** -0.5), 0.2]))
+        out.append((B, H, N, d, str(rng.choice(["f16", "bf16"])), bool(rng.integers(0, 2)),
+                    float(rng.choice([1.0, 2.0])), round(sc, 6)))
+    return out
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype,causal,sigma,scale", _random_bwd_shapes(16))
+def test_bwd_random_shapes(B, H, N, d, dtype, causal, sigma, scale):
+    run(B, H, N, d, dtype, causal, seed=300 + N, sigma_qk=sigma, scale=scale)
