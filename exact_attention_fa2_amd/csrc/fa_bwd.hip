@@ -22,7 +22,9 @@ int64_t bwd_bytes(int B, int H, int N) {
 //    (three); d = 96 in two passes, dV then dK.
 //  * dQ with K/V tiles by LDS-DMA: 8 waves at d = 128, 4 at d = 64 (dO
 //    fragments in LDS, three waves per SIMD); the register-staged kernel at
-//    d = 96.
+//    d = 96 and 256.
+//  * d = 256 takes the d = 96 sequence at one wave per SIMD: the two dK/dV
+//    passes and the dQ kernel each hold 128 accumulator registers.
 // Every kernel orders its blocks key/query block major, head minor.
 // Measured per backward, same GPU, against the earlier two-pass dK/dV
 // (d = 128) or fused dK/dV with K/V fragments in registers (d = 64), the
@@ -39,7 +41,7 @@ int launch(const BwdArgs& a, hipStream_t st) {
   if (gdot > (INT64_C(1) << 31) - 1 || gk > (INT64_C(1) << 31) - 1 || gq > (INT64_C(1) << 31) - 1)
     return FA_ERR_DIM;
   (void)hipGetLastError();
-  if constexpr (D == 96) {
+  if constexpr (D == 96 || D == 256) {
     hipLaunchKernelGGL((fa_bwd_dot_kernel<D, DT>), dim3((unsigned)gdot), dim3(256), 0, st, a);
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, DT, CAUSAL, BWD_DV>), dim3((unsigned)gk), dim3(256), 0, st, a);
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, DT, CAUSAL, BWD_DK>), dim3((unsigned)gk), dim3(256), 0, st, a);
@@ -68,7 +70,8 @@ int pick_d(const BwdArgs& a, int d, bool causal, hipStream_t st) {
     case 64: return pick_c<64, DT>(a, causal, st);
     case 96: return pick_c<96, DT>(a, causal, st);
     case 128: return pick_c<128, DT>(a, causal, st);
-    default: return FA_ERR_UNSUPPORTED;  // d = 256: the dK/dV accumulators do not fit
+    case 256: return pick_c<256, DT>(a, causal, st);
+    default: return FA_ERR_UNSUPPORTED;
   }
 }
 
@@ -124,7 +127,6 @@ int check_bwd(const void* q, const void* k, const void* v, const void* o, const 
               int64_t max_rows, int64_t* elems) {
   int rc = check_problem(B, H, N, d, scale, dtype, elems);
   if (rc != FA_OK) return rc;
-  if (d == 256) return FA_ERR_UNSUPPORTED;
   if (*elems == 0) return FA_OK;
   if (max_rows > 0 && *elems / d > max_rows) return FA_ERR_TOO_LARGE;
   if (!q || !k || !v || !o || !do_ || !lse || !dq || !dk || !dv) return FA_ERR_NULL;

@@ -7,9 +7,9 @@
 //   dK = scale · dSᵀ Q,  dQ = scale · dS K.
 //
 // MI355X layout (our design), no atomics: two kernels at d = 64 and 128 (dQ,
-// which also forms D_i, then dK/dV), four at d = 96. Blocks are ordered key
-// or query block major, head minor.
-//  * fa_bwd_dot_kernel (d = 96): D_i in fp32. At d = 64 and 128 the dQ
+// which also forms D_i, then dK/dV), four at d = 96 and 256. Blocks are
+// ordered key or query block major, head minor.
+//  * fa_bwd_dot_kernel (d = 96, 256): D_i in fp32. At d = 64 and 128 the dQ
 //    kernel forms D_i for its own rows and stores it; it runs first.
 //  * fa_bwd_dkdv_wide_kernel (d = 64, 128): one workgroup per block of keys,
 //    each wave owning 32 keys; 64-query tiles of Q, dO, LSE and D stream
@@ -17,11 +17,11 @@
 //    so P and dS are directly the B operand of dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS,
 //    whose A operands (dOᵀ, Qᵀ) come from the row-major LDS tiles through the
 //    transposing LDS read.
-//  * fa_bwd_dkdv_kernel (d = 96): the same as two passes, dV then dK, with
-//    K and V fragments in registers.
+//  * fa_bwd_dkdv_kernel (d = 96, 256): the same as two passes, dV then dK,
+//    with K and V fragments in registers.
 //  * fa_bwd_dq_kernel (d = 64, 128): the mirror image with the query in the
 //    lane (like the forward): Pᵀ = exp2(Sᵀ c - LSE log2 e), dPᵀ = V dOᵀ,
-//    dQᵀ += Kᵀ dSᵀ; fa_bwd_dq_staged_kernel is the same for d = 96.
+//    dQᵀ += Kᵀ dSᵀ; fa_bwd_dq_staged_kernel is the same for d = 96 and 256.
 #pragma once
 #include "fa_fwd_kernel.h"
 #include "fa_fwd_split.h"
@@ -85,7 +85,10 @@ __global__ __launch_bounds__(256) void fa_bwd_dot_kernel(const BwdArgs a) {
 
 template <int D>
 struct BwdSmem {
-  static constexpr int BQ = 64;        // query rows per tile (dK/dV kernel)
+  // query rows per tile (two-pass dK/dV kernel); 32 at d = 256, which halves
+  // the registers that stage the next tile (64 -> 32) and keeps the dK pass
+  // free of spills at one wave per SIMD
+  static constexpr int BQ = D == 256 ? 32 : 64;
   static constexpr int STR = D + 16;   // padded row (halves)
   static constexpr int TILE = BQ * STR;
   // per stage: Q tile, dO tile, LSE·log2e, D
@@ -108,12 +111,18 @@ __device__ __forceinline__ f32x16 load_rowvals(const float* base, int hh) {
 
 // ---- dK, dV in two passes: one workgroup per 128 keys ----
 // PART BWD_DV computes only dV (no V fragments, no dP), PART BWD_DK only dK.
-// Each pass then fits two waves per SIMD with the K and V fragments in
-// registers (d = 96, whose 12 chunks per row do not split over the
-// single-pass kernel's LDS-DMA).
+// At d = 96 (whose 12 chunks per row do not split over the single-pass
+// kernel's LDS-DMA) each pass then fits two waves per SIMD with the K and V
+// fragments in registers. At d = 256 a pass holds 128 accumulator registers
+// besides 64 of K (and 64 of V) fragments: one wave per SIMD, with the
+// accumulation registers as overflow, and 69 KB of LDS per workgroup.
 enum { BWD_DV = 1, BWD_DK = 2 };
+template <int D>
+constexpr int bwd_pass_min_blocks() {
+  return D == 256 ? 1 : 2;
+}
 template <int D, int DT, bool CAUSAL, int PART>
-__global__ __launch_bounds__(256, 2) void fa_bwd_dkdv_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(256, (bwd_pass_min_blocks<D>())) void fa_bwd_dkdv_kernel(const BwdArgs a) {
   static_assert(PART == BWD_DV || PART == BWD_DK, "one of the two passes");
   constexpr bool WANT_DV = PART == BWD_DV, WANT_DK = PART == BWD_DK;
   constexpr int NW = 4, NT = 256, KK = D / 16, DB = D / 32;
@@ -765,9 +774,11 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_bwd_dq_kernel(con
   }
 }
 
-// ---- dQ at d = 96: K/V tiles staged through registers into padded rows ----
-// (96 halves per row split into 12 chunks, which the XOR swizzle of the
-// LDS-DMA layout does not cover). Otherwise as fa_bwd_dq_kernel.
+// ---- dQ at d = 96 and 256: K/V tiles staged through registers into padded
+// rows (96 halves per row split into 12 chunks, which the XOR swizzle of the
+// LDS-DMA layout does not cover; at 256 the swizzle is not laid out either).
+// Otherwise as fa_bwd_dq_kernel. At d = 256 it runs at one wave per SIMD
+// (Q and dO fragments 128 registers, the dQ accumulator 128).
 template <int D, int DT, bool CAUSAL, int NW>
 __global__ __launch_bounds__(NW * 64) void fa_bwd_dq_staged_kernel(const BwdArgs a) {
   constexpr int NT = NW * 64, BR = NW * 32, BC = 64, KK = D / 16, DB = D / 32, KB = BC / 32;

@@ -198,7 +198,8 @@ def test_bwd_argument_errors(L):
     assert call(dk=A) == ALIAS            # dk over q
     assert call(dv=A + 448 * MB) == ALIAS  # dv over dk
     assert call(ws=A + 320 * MB) == ALIAS  # workspace over lse
-    assert call(d=256) == UNSUP
+    assert call(d=32) == UNSUP
+    assert call(d=256, q=None) == NULL  # d = 256 accepted
     assert call(scale=float("nan")) == SCALE
     assert call(N=0, q=None) == OK
     assert L.fa_bwd_workspace_bytes(2, 3, 100, 64) >= 2 * 3 * 100 * 4
@@ -263,7 +264,8 @@ def test_bwd_noalloc_argument_errors(L):
     assert call(dq=A + 384 * MB + 2) == ALIGN
     assert call(dk=A) == ALIAS
     assert call(dv=A + 448 * MB) == ALIAS
-    assert call(d=256) == UNSUP
+    assert call(d=32) == UNSUP
+    assert call(d=256, q=None) == NULL  # d = 256 accepted
     assert call(scale=float("inf")) == SCALE
     assert call(N=0, q=None) == OK
     assert call() == DEVICE  # valid arguments, no GPU in this process

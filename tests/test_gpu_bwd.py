@@ -56,7 +56,8 @@ def run(B, H, N, d, dtype, causal, seed, sigma_qk=1.0, scale=None):
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N,d,dtype", [(1, 64, "f16"), (64, 64, "bf16"), (200, 64, "f16"), (400, 64, "bf16"),
                                        (129, 128, "f16"), (300, 128, "bf16"), (97, 96, "f16"), (1000, 64, "f16"),
-                                       (700, 128, "bf16"), (333, 96, "bf16"), (1030, 96, "f16")])
+                                       (700, 128, "bf16"), (333, 96, "bf16"), (1030, 96, "f16"),
+                                       (130, 256, "f16"), (300, 256, "bf16")])
 def test_bwd_matches_oracle(N, d, dtype, causal):
     run(2, 2, N, d, dtype, causal, seed=N + d)
 
@@ -71,6 +72,15 @@ def test_bwd_d128_negative_scale(causal):
     # d = 128 folds the sign of the scale into K and into dK's final multiply
     run(1, 2, 300, 128, "bf16", causal, seed=11, scale=-0.09)
     run(1, 1, 513, 128, "f16", causal, seed=12, scale=-0.2)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_d256(causal):
+    # one wave per SIMD, accumulation registers as overflow; several key and
+    # query blocks with a ragged tail, and a negative scale (K read
+    # sign-flipped, dK multiplied by it at the end)
+    run(1, 2, 517, 256, "bf16", causal, seed=13, scale=-0.0625)
+    run(2, 1, 1100, 256, "f16", causal, seed=14, sigma_qk=2.0)
 
 
 def test_bwd_deterministic():
