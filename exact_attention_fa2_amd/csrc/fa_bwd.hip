@@ -16,6 +16,19 @@ int64_t bwd_bytes(int B, int H, int N) {
   return ((int64_t)B * H * N * 4 + 255) / 256 * 256;  // D_i in fp32
 }
 
+// Compute units of the current device, queried once (256 on MI355X; 0 if
+// the query fails, which keeps the two-kernel sequence).
+int cu_count() {
+  static const int n = [] {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    return cus;
+  }();
+  return n;
+}
+
 // Kernels per head dim, each at the occupancy its registers allow:
 //  * dK/dV in one pass with V fragments parked in LDS: d = 128 in 8-wave,
 //    256-key blocks (two waves per SIMD), d = 64 in 4-wave, 128-key blocks
@@ -25,6 +38,14 @@ int64_t bwd_bytes(int B, int H, int N) {
 //    d = 96 and 256.
 //  * d = 256 takes the d = 96 sequence at one wave per SIMD: the two dK/dV
 //    passes and the dQ kernel each hold 128 accumulator registers.
+//  * d = 64 and 128 with at most one dQ block per CU (B*H*ceil(N/(32 QNW))
+//    <= CUs): D_i by fa_bwd_dot_kernel, then one joint grid that interleaves
+//    the dQ and dK/dV blocks, so both halves share the chip instead of each
+//    leaving half of it idle. Kernel-only, warm, bf16 d = 64, same GPU: B1 H4
+//    N4096 151 -> 107 us (causal 159 -> 104), B1 H2 N8192 297 -> 207, B2 H4
+//    N400 24.7 -> 17.6, B1 H16 N1024 44.3 -> 31.5; 256 dQ blocks: B2 H8 N2048
+//    83.9 -> 75.6, B4 H16 N512 29.9 -> 28.5; 512 (N=400 x128 heads): 35.5 ->
+//    43.6, so the larger grids keep the sequence.
 // Every kernel orders its blocks key/query block major, head minor.
 // Measured per backward, same GPU, against the earlier two-pass dK/dV
 // (d = 128) or fused dK/dV with K/V fragments in registers (d = 64), the
@@ -47,6 +68,14 @@ int launch(const BwdArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, DT, CAUSAL, BWD_DK>), dim3((unsigned)gk), dim3(256), 0, st, a);
     hipLaunchKernelGGL((fa_bwd_dq_staged_kernel<D, DT, CAUSAL, QNW>), dim3((unsigned)gq), dim3(QNW * 64), 0, st, a);
   } else {
+    static_assert(QNW == bwd_joint_waves<D>(), "the joint grid pairs equal dQ and dK/dV grids");
+    if (gq <= cu_count()) {
+      // each half alone would fill at most one workgroup per CU: D_i first,
+      // then the dQ and dK/dV blocks side by side in one grid
+      hipLaunchKernelGGL((fa_bwd_dot_kernel<D, DT>), dim3((unsigned)gdot), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((fa_bwd_joint_kernel<D, DT, CAUSAL>), dim3((unsigned)(2 * gq)), dim3(QNW * 64), 0, st, a);
+      return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+    }
     // dQ first: it also forms and stores D_i, which dK/dV reads
     hipLaunchKernelGGL((fa_bwd_dq_kernel<D, DT, CAUSAL, QNW>), dim3((unsigned)gq), dim3(QNW * 64), 0, st, a);
     if constexpr (D == 128) {

@@ -22,6 +22,8 @@
 //  * fa_bwd_dq_kernel (d = 64, 128): the mirror image with the query in the
 //    lane (like the forward): Pᵀ = exp2(Sᵀ c - LSE log2 e), dPᵀ = V dOᵀ,
 //    dQᵀ += Kᵀ dSᵀ; fa_bwd_dq_staged_kernel is the same for d = 96 and 256.
+//  * fa_bwd_joint_kernel (d = 64, 128, small grids): the dQ and dK/dV blocks
+//    in one launch, after fa_bwd_dot_kernel.
 #pragma once
 #include "fa_fwd_kernel.h"
 #include "fa_fwd_split.h"
@@ -346,8 +348,12 @@ __global__ __launch_bounds__(256, (bwd_pass_min_blocks<D>())) void fa_bwd_dkdv_k
 //    XOR-swizzled (lds_off<D, 0>), double-buffered and shared by the NW waves.
 // A negative scale flips the sign of K (so S keeps the sign of scale·q·k)
 // and multiplies dK at the end; Q is used as stored.
-template <int D, int DT, bool CAUSAL, int NW, int MINB>
-__global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv_wide_kernel(const BwdArgs a) {
+template <int D, int NW>
+constexpr int dkdv_wide_smem_halves() {
+  return 2 * (2 * 64 * D + 2 * 64 * 2) + NW * (D / 16) * 64 * 8;
+}
+template <int D, int DT, bool CAUSAL, int NW>
+__device__ __forceinline__ void dkdv_wide_body(const BwdArgs& a, const int bid, uint16_t* smem) {
   constexpr int KK = D / 16, DB = D / 32, KW = 32 * NW, BQ = 64, CPR = D / 8;
   constexpr int TILE = BQ * D;                   // halves per unpadded Q or dO tile
   constexpr int STAGE = 2 * TILE + 2 * BQ * 2;   // Q, dO, then the row terms (fp32)
@@ -355,7 +361,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv_wide_kernel(const B
   static_assert(LOADS % NW == 0, "tile loads split evenly over the waves");
   constexpr int LPW = LOADS / NW;
   constexpr int VFRAG = KK * 64;                 // u32x4 per wave
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE + NW * VFRAG * 8];
+  static_assert(2 * STAGE + NW * VFRAG * 8 == dkdv_wide_smem_halves<D, NW>(), "LDS size");
 
   // block order: key block major, head minor. Causal blocks then start
   // longest first across all heads (a head-major order leaves the long
@@ -363,7 +369,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv_wide_kernel(const B
   // XCDs every block of a head lands on one XCD, sharing its Q/dO in L2.
   const int nkb = (a.N + KW - 1) / KW;
   const int BH = a.B * a.H;
-  const int kblk = blockIdx.x / BH, bh = blockIdx.x - kblk * BH;
+  const int kblk = bid / BH, bh = bid - kblk * BH;
   if (kblk >= nkb) return;
   const int64_t off = (int64_t)bh * a.N * D;
   const uint16_t* Qg = a.q + off;
@@ -569,13 +575,23 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv_wide_kernel(const B
   }
 }
 
+template <int D, int DT, bool CAUSAL, int NW, int MINB>
+__global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv_wide_kernel(const BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[dkdv_wide_smem_halves<D, NW>()];
+  dkdv_wide_body<D, DT, CAUSAL, NW>(a, blockIdx.x, smem);
+}
+
 // ---- dQ: one workgroup per NW*32 queries (query in the lane) ----
 // NW waves of 32 query rows per workgroup (8 at d = 128, 4 at d = 64). K/V
 // tiles arrive by LDS-DMA into unpadded, XOR-swizzled rows (no staging
 // registers); at d = 64 each wave also parks its dO fragments in its own LDS
 // slice, which brings the kernel to three waves per SIMD.
-template <int D, int DT, bool CAUSAL, int NW>
-__global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_bwd_dq_kernel(const BwdArgs a) {
+template <int D, int NW>
+constexpr int dq_smem_halves() {
+  return 4 * 64 * D + (D == 64 ? NW * (D / 16) * 64 * 8 : 0);
+}
+template <int D, int DT, bool CAUSAL, int NW, bool DI>
+__device__ __forceinline__ void dq_body(const BwdArgs& a, const int bid, uint16_t* smem) {
   static_assert(D == 64 || D == 128, "swizzled LDS-DMA tiles: d = 64 or 128");
   constexpr int BR = NW * 32, BC = 64, KK = D / 16, DB = D / 32, KB = BC / 32, CPR = D / 8;
   constexpr int TILE = BC * D;                   // halves per unpadded K or V tile
@@ -584,13 +600,13 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_bwd_dq_kernel(con
   constexpr int LPW = LOADS / NW;
   constexpr bool GL = D == 64;                   // dO fragments parked in LDS
   constexpr int GFRAG = KK * 64;                 // u32x4 per wave
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE + (GL ? NW * GFRAG * 8 : 0)];
+  static_assert(4 * TILE + (GL ? NW * GFRAG * 8 : 0) == dq_smem_halves<D, NW>(), "LDS size");
 
   // block order: query block major (causal: longest first across all
   // heads), head minor, as in fa_bwd_dkdv_wide_kernel
   const int nqb = (a.N + BR - 1) / BR;
   const int BH = a.B * a.H;
-  const int qblk0 = blockIdx.x / BH, bh = blockIdx.x - qblk0 * BH;
+  const int qblk0 = bid / BH, bh = bid - qblk0 * BH;
   if (qblk0 >= nqb) return;
   const int qblk = CAUSAL ? nqb - 1 - qblk0 : qblk0;
   const int64_t off = (int64_t)bh * a.N * D;
@@ -606,8 +622,9 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_bwd_dq_kernel(con
   const int qrow = qw0 + l32;
 
   // Q and dO fragments of this lane's row (its half of the d columns), and
-  // D_i = <dO_i, O_i> from the same half of O plus the partner lane's half.
-  // D_i is also stored for the dK/dV kernel, which runs after this one.
+  // (DI) D_i = <dO_i, O_i> from the same half of O plus the partner lane's
+  // half, stored for the dK/dV kernel, which runs after this one; without
+  // DI, D_i is read from the row terms fa_bwd_dot_kernel wrote.
   u32x4 qf[KK], gf[GL ? 1 : KK];
   u32x4* gl = (u32x4*)(smem + 4 * TILE) + w * GFRAG;
   const uint16_t* Og = a.o + off;
@@ -617,7 +634,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_bwd_dq_kernel(con
     const int rr = min(qrow, N - 1);
     const u32x4 x = *(const u32x4*)(Qg + (int64_t)rr * D + 16 * kk + 8 * hh);
     const u32x4 y = *(const u32x4*)(Gg + (int64_t)rr * D + 16 * kk + 8 * hh);
-    const u32x4 ov = *(const u32x4*)(Og + (int64_t)rr * D + 16 * kk + 8 * hh);
+    const u32x4 ov = DI ? *(const u32x4*)(Og + (int64_t)rr * D + 16 * kk + 8 * hh) : u32x4{0u, 0u, 0u, 0u};
     qf[kk] = (qrow < N ? x : u32x4{0u, 0u, 0u, 0u}) ^ a.qsign;
     const u32x4 g = qrow < N ? y : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
@@ -631,8 +648,13 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_bwd_dq_kernel(con
       gf[kk] = g;
   }
   const float lq = qrow < N ? a.lse[(int64_t)bh * N + qrow] * kLog2e : INFINITY;
-  const float dq_row = dpart + xor_lane32(dpart);
-  if (hh == 0 && qrow < N) a.dvec[(int64_t)bh * N + qrow] = dq_row;
+  float dq_row;
+  if constexpr (DI) {
+    dq_row = dpart + xor_lane32(dpart);
+    if (hh == 0 && qrow < N) a.dvec[(int64_t)bh * N + qrow] = dq_row;
+  } else {
+    dq_row = qrow < N ? a.dvec[(int64_t)bh * N + qrow] : 0.f;
+  }
 
   f32x16 dqacc[DB];
 #pragma unroll
@@ -772,6 +794,35 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_bwd_dq_kernel(con
         *(u32x2*)(dqr + db * 32 + 8 * g4 + 4 * hh) = x;
       }
   }
+}
+
+template <int D, int DT, bool CAUSAL, int NW>
+__global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_bwd_dq_kernel(const BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[dq_smem_halves<D, NW>()];
+  dq_body<D, DT, CAUSAL, NW, true>(a, blockIdx.x, smem);
+}
+
+// ---- dQ and dK/dV blocks in one grid (d = 64, 128) ----
+// For grids that leave the chip half empty: block 2i is dQ block i (D_i read
+// from fa_bwd_dot_kernel, which runs first), block 2i + 1 is dK/dV block i,
+// so the two halves of the backward run side by side instead of one after
+// the other. NW waves per workgroup as in the separate kernels (the dQ and
+// dK/dV grids then have the same number of blocks), LDS the larger of the two.
+template <int D>
+constexpr int bwd_joint_waves() {
+  return D == 128 ? 8 : 4;
+}
+template <int D, int DT, bool CAUSAL>
+__global__ __launch_bounds__(bwd_joint_waves<D>() * 64, D == 64 ? 3 : 1)
+void fa_bwd_joint_kernel(const BwdArgs a) {
+  constexpr int NW = bwd_joint_waves<D>();
+  constexpr int H1 = dq_smem_halves<D, NW>(), H2 = dkdv_wide_smem_halves<D, NW>();
+  __shared__ __attribute__((aligned(16))) uint16_t smem[H1 > H2 ? H1 : H2];
+  const int bid = blockIdx.x;
+  if (bid & 1)
+    dkdv_wide_body<D, DT, CAUSAL, NW>(a, bid >> 1, smem);
+  else
+    dq_body<D, DT, CAUSAL, NW, false>(a, bid >> 1, smem);
 }
 
 // ---- dQ at d = 96 and 256: K/V tiles staged through registers into padded

@@ -93,32 +93,52 @@ def test_bwd_deterministic():
     assert all(torch.equal(x, y) for x, y in zip(g1, g2))
 
 
-@pytest.mark.parametrize("name", ["n400_batched", "n4096", "n8192_causal"])
-def test_bwd_workload_sampled_heads(name):
-    # the backward at the benchmarked size, launched exactly as bench.py times
-    # it; whole (batch, head) slices compared with the oracle (first, last and
-    # one seeded head)
-    w = inputs.WORKLOADS[name]
-    print(f"[fa_bwd] workload {name}: B{w.B} H{w.H} N{w.N} d{w.d} {w.dtype} causal={w.causal}", flush=True)
-    q, k, v = inputs.make_qkv(w.B, w.H, w.N, w.d, w.dtype, 0, w.sigma_qk, w.sigma_v)
-    do = inputs.make_like(q, 1000)
+def run_sampled_heads(B, H, N, d, dtype, causal, seed, scale, sigma_qk=1.0, sigma_v=1.0):
+    # all heads on the GPU, whole (batch, head) slices compared with the
+    # oracle: the first, the last and one seeded head
+    q, k, v = inputs.make_qkv(B, H, N, d, dtype, seed, sigma_qk, sigma_v)
+    do = inputs.make_like(q, seed + 1000)
     qg, kg, vg, dog = (t.cuda() for t in (q, k, v, do))
-    o, lse = fa.attention(qg, kg, vg, causal=w.causal, scale=w.scale)
-    dq, dk, dv = fa.attention_backward(qg, kg, vg, o, lse, dog, causal=w.causal, scale=w.scale)
+    o, lse = fa.attention(qg, kg, vg, causal=causal, scale=scale)
+    dq, dk, dv = fa.attention_backward(qg, kg, vg, o, lse, dog, causal=causal, scale=scale)
     torch.cuda.synchronize()
     grads = [P.to64(g) for g in (dq, dk, dv)]
     assert all(np.isfinite(g).all() for g in grads)
     rng = np.random.default_rng(7)
-    heads = {(0, 0), (w.B - 1, w.H - 1), (int(rng.integers(w.B)), int(rng.integers(w.H)))}
+    heads = {(0, 0), (B - 1, H - 1), (int(rng.integers(B)), int(rng.integers(H)))}
     for b, h in sorted(heads):
-        qd, kd, vd, dod = (P.decode(x[b:b + 1, h:h + 1], w.dtype) for x in (q, k, v, do))
-        refs = oracle.attention_bwd(qd, kd, vd, dod, w.scale, w.causal)
+        qd, kd, vd, dod = (P.decode(x[b:b + 1, h:h + 1], dtype) for x in (q, k, v, do))
+        refs = oracle.attention_bwd(qd, kd, vd, dod, scale, causal)
         amax = lambda x: float(np.abs(x).max())
-        floor = 2.0 ** -20 * w.d * amax(dod) * amax(vd) * w.d * max(amax(qd), amax(kd)) * abs(w.scale)
+        floor = 2.0 ** -20 * d * amax(dod) * amax(vd) * d * max(amax(qd), amax(kd)) * abs(scale)
         rel = {}
         for gname, g, r in zip(("dq", "dk", "dv"), grads, refs):
-            rel[gname] = gate_grad(g[b:b + 1, h:h + 1], r, w.dtype, f"{gname} head ({b},{h})", floor)
+            rel[gname] = gate_grad(g[b:b + 1, h:h + 1], r, dtype, f"{gname} head ({b},{h})", floor)
         print(f"  head ({b},{h}) rel errors", {k2: f"{v2:.2e}" for k2, v2 in rel.items()}, flush=True)
+
+
+@pytest.mark.parametrize("name", ["n400_batched", "n4096", "n8192_causal"])
+def test_bwd_workload_sampled_heads(name):
+    # the backward at the benchmarked size, launched exactly as bench.py times it
+    w = inputs.WORKLOADS[name]
+    print(f"[fa_bwd] workload {name}: B{w.B} H{w.H} N{w.N} d{w.d} {w.dtype} causal={w.causal}", flush=True)
+    run_sampled_heads(w.B, w.H, w.N, w.d, w.dtype, w.causal, 0, w.scale, w.sigma_qk, w.sigma_v)
+
+
+# Both sides of the switch between the joint grid (at most one dQ block per
+# CU, 256 on MI355X: dQ blocks are 128 query rows at d = 64, 256 at d = 128)
+# and the two-kernel sequence.
+@pytest.mark.parametrize("B,H,N,d,dtype,causal", [
+    (1, 64, 512, 64, "f16", True),     # 256 dQ blocks: joint
+    (1, 65, 512, 64, "f16", True),     # 260: sequence
+    (2, 64, 300, 64, "bf16", False),   # 384: sequence
+    (1, 32, 2048, 128, "bf16", True),  # 256: joint
+    (1, 33, 2048, 128, "f16", False),  # 264: sequence
+    (1, 3, 4100, 64, "bf16", False),   # 99 (ragged last block): joint
+])
+def test_bwd_joint_and_sequence_paths(B, H, N, d, dtype, causal):
+    print(f"[fa_bwd] paths B{B} H{H} N{N} d{d} {dtype} causal={causal}", flush=True)
+    run_sampled_heads(B, H, N, d, dtype, causal, N + H, d ** -0.5)
 
 
 def _random_bwd_shapes(n, seed=2027):
