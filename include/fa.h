@@ -138,9 +138,10 @@ int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *l
  *                     are ignored. It holds the fp32 row terms D_i = <dO_i, O_i>.
  * Head dims 64, 96, 128 and 256. The kernels enqueued on `stream`: at d = 64
  * and 128, dQ (parallel over query blocks; it also forms D_i) then dK/dV
- * (parallel over key blocks); at d = 96 and 256, D_i, then dK/dV as two
- * passes (dV, then dK), then dQ (d = 256 at one wave per SIMD). There are no
- * atomics, so results are deterministic.
+ * (parallel over key blocks), or, when there is at most one dQ block per
+ * compute unit, D_i and then one grid holding both kernels' blocks; at d = 96
+ * and 256, D_i, then dK/dV as two passes (dV, then dK), then dQ (d = 256 at
+ * one wave per SIMD). There are no atomics, so results are deterministic.
  */
 int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *do_,
            const float *lse, void *dq, void *dk, void *dv, void *workspace,
