@@ -38,6 +38,9 @@ int cu_count() {
 //    d = 96 and 256.
 //  * d = 256 takes the d = 96 sequence at one wave per SIMD: the two dK/dV
 //    passes and the dQ kernel each hold 128 accumulator registers.
+//  * d = 96 and 256 with at most one block of each kind per CU: after D_i,
+//    one joint grid of the dQ, dV-pass and dK-pass blocks (d = 96 B1 H4
+//    N2048 139 -> 53 us, d = 256 B1 H4 N2048 382 -> 158 us, same GPU).
 //  * d = 64 and 128 with at most one dQ block per CU (B*H*ceil(N/(32 QNW))
 //    <= CUs): D_i by fa_bwd_dot_kernel, then one joint grid that interleaves
 //    the dQ and dK/dV blocks, so both halves share the chip instead of each
@@ -64,6 +67,11 @@ int launch(const BwdArgs& a, hipStream_t st) {
   (void)hipGetLastError();
   if constexpr (D == 96 || D == 256) {
     hipLaunchKernelGGL((fa_bwd_dot_kernel<D, DT>), dim3((unsigned)gdot), dim3(256), 0, st, a);
+    if (gk <= cu_count()) {
+      // the dQ, dV-pass and dK-pass blocks side by side in one grid
+      hipLaunchKernelGGL((fa_bwd_joint_staged_kernel<D, DT, CAUSAL>), dim3((unsigned)(3 * gk)), dim3(256), 0, st, a);
+      return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+    }
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, DT, CAUSAL, BWD_DV>), dim3((unsigned)gk), dim3(256), 0, st, a);
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, DT, CAUSAL, BWD_DK>), dim3((unsigned)gk), dim3(256), 0, st, a);
     hipLaunchKernelGGL((fa_bwd_dq_staged_kernel<D, DT, CAUSAL, QNW>), dim3((unsigned)gq), dim3(QNW * 64), 0, st, a);

@@ -22,8 +22,9 @@
 //  * fa_bwd_dq_kernel (d = 64, 128): the mirror image with the query in the
 //    lane (like the forward): Pᵀ = exp2(Sᵀ c - LSE log2 e), dPᵀ = V dOᵀ,
 //    dQᵀ += Kᵀ dSᵀ; fa_bwd_dq_staged_kernel is the same for d = 96 and 256.
-//  * fa_bwd_joint_kernel (d = 64, 128, small grids): the dQ and dK/dV blocks
-//    in one launch, after fa_bwd_dot_kernel.
+//  * fa_bwd_joint_kernel (d = 64, 128) and fa_bwd_joint_staged_kernel (d =
+//    96, 256), for small grids: the blocks of the dQ and dK/dV kernels in one
+//    launch, after fa_bwd_dot_kernel.
 #pragma once
 #include "fa_fwd_kernel.h"
 #include "fa_fwd_split.h"
@@ -124,7 +125,7 @@ constexpr int bwd_pass_min_blocks() {
   return D == 256 ? 1 : 2;
 }
 template <int D, int DT, bool CAUSAL, int PART>
-__global__ __launch_bounds__(256, (bwd_pass_min_blocks<D>())) void fa_bwd_dkdv_kernel(const BwdArgs a) {
+__device__ __forceinline__ void dkdv_pass_body(const BwdArgs& a, const int bid, uint16_t* smem) {
   static_assert(PART == BWD_DV || PART == BWD_DK, "one of the two passes");
   constexpr bool WANT_DV = PART == BWD_DV, WANT_DK = PART == BWD_DK;
   constexpr int NW = 4, NT = 256, KK = D / 16, DB = D / 32;
@@ -132,12 +133,11 @@ __global__ __launch_bounds__(256, (bwd_pass_min_blocks<D>())) void fa_bwd_dkdv_k
   constexpr int BQ = SM::BQ, STR = SM::STR;
   constexpr int CH = BQ * D / 8 / NT;  // 16-byte chunks per thread per tile
   static_assert(BQ * D / 8 % NT == 0, "tile must split evenly");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SM::STAGE_HALVES];
 
   // block order as in fa_bwd_dkdv_wide_kernel: key block major, head minor
   const int nkb = (a.N + 127) / 128;
   const int BH = a.B * a.H;
-  const int kblk = blockIdx.x / BH, bh = blockIdx.x - kblk * BH;
+  const int kblk = bid / BH, bh = bid - kblk * BH;
   if (kblk >= nkb) return;
   const int64_t off = (int64_t)bh * a.N * D;
   const uint16_t* Qg = a.q + off;
@@ -334,6 +334,12 @@ __global__ __launch_bounds__(256, (bwd_pass_min_blocks<D>())) void fa_bwd_dkdv_k
         }
       }
   }
+}
+
+template <int D, int DT, bool CAUSAL, int PART>
+__global__ __launch_bounds__(256, (bwd_pass_min_blocks<D>())) void fa_bwd_dkdv_kernel(const BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BwdSmem<D>::STAGE_HALVES];
+  dkdv_pass_body<D, DT, CAUSAL, PART>(a, blockIdx.x, smem);
 }
 
 // ---- dK and dV in one pass: NW waves, 32 NW keys per workgroup ----
@@ -831,16 +837,15 @@ void fa_bwd_joint_kernel(const BwdArgs a) {
 // Otherwise as fa_bwd_dq_kernel. At d = 256 it runs at one wave per SIMD
 // (Q and dO fragments 128 registers, the dQ accumulator 128).
 template <int D, int DT, bool CAUSAL, int NW>
-__global__ __launch_bounds__(NW * 64) void fa_bwd_dq_staged_kernel(const BwdArgs a) {
+__device__ __forceinline__ void dq_staged_body(const BwdArgs& a, const int bid, uint16_t* smem) {
   constexpr int NT = NW * 64, BR = NW * 32, BC = 64, KK = D / 16, DB = D / 32, KB = BC / 32;
   constexpr int CH = BC * D / 8 / NT;
   static_assert(BC * D / 8 % NT == 0, "tile must split evenly");
   using SM = FwdSmem<D, BC>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SM::STAGE];
 
   const int nqb = (a.N + BR - 1) / BR;
   const int BH = a.B * a.H;
-  const int qblk0 = blockIdx.x / BH, bh = blockIdx.x - qblk0 * BH;
+  const int qblk0 = bid / BH, bh = bid - qblk0 * BH;
   if (qblk0 >= nqb) return;
   const int qblk = CAUSAL ? nqb - 1 - qblk0 : qblk0;  // longest first
   const int64_t off = (int64_t)bh * a.N * D;
@@ -998,6 +1003,31 @@ __global__ __launch_bounds__(NW * 64) void fa_bwd_dq_staged_kernel(const BwdArgs
         *(u32x2*)(dqr + db * 32 + 8 * g4 + 4 * hh) = x;
       }
   }
+}
+
+// two workgroups per CU at d = 96 (228-236 VGPRs; left to itself the
+// compiler may take more and halve the occupancy), one at d = 256
+template <int D, int DT, bool CAUSAL, int NW>
+__global__ __launch_bounds__(NW * 64, (bwd_pass_min_blocks<D>())) void fa_bwd_dq_staged_kernel(const BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * FwdSmem<D, 64>::STAGE];
+  dq_staged_body<D, DT, CAUSAL, NW>(a, blockIdx.x, smem);
+}
+
+// ---- the d = 96 and 256 sequence in one grid, for small grids ----
+// Block 3i is dQ block i, 3i + 1 dV-pass block i, 3i + 2 dK-pass block i
+// (128 queries or keys each, 4 waves), after fa_bwd_dot_kernel; LDS the
+// largest of the three.
+template <int D, int DT, bool CAUSAL>
+__global__ __launch_bounds__(256, (bwd_pass_min_blocks<D>())) void fa_bwd_joint_staged_kernel(const BwdArgs a) {
+  constexpr int H1 = 2 * FwdSmem<D, 64>::STAGE, H2 = 2 * BwdSmem<D>::STAGE_HALVES;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[H1 > H2 ? H1 : H2];
+  const int bid = blockIdx.x, i = bid / 3, kind = bid - 3 * i;
+  if (kind == 0)
+    dq_staged_body<D, DT, CAUSAL, 4>(a, i, smem);
+  else if (kind == 1)
+    dkdv_pass_body<D, DT, CAUSAL, BWD_DV>(a, i, smem);
+  else
+    dkdv_pass_body<D, DT, CAUSAL, BWD_DK>(a, i, smem);
 }
 
 }  // namespace fa

@@ -141,7 +141,9 @@ int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *l
  * (parallel over key blocks), or, when there is at most one dQ block per
  * compute unit, D_i and then one grid holding both kernels' blocks; at d = 96
  * and 256, D_i, then dK/dV as two passes (dV, then dK), then dQ (d = 256 at
- * one wave per SIMD). There are no atomics, so results are deterministic.
+ * one wave per SIMD), the three again in one grid when there is at most one
+ * block of each per compute unit. There are no atomics, so results are
+ * deterministic.
  */
 int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *do_,
            const float *lse, void *dq, void *dk, void *dv, void *workspace,

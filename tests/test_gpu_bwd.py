@@ -126,8 +126,8 @@ def test_bwd_workload_sampled_heads(name):
 
 
 # Both sides of the switch between the joint grid (at most one dQ block per
-# CU, 256 on MI355X: dQ blocks are 128 query rows at d = 64, 256 at d = 128)
-# and the two-kernel sequence.
+# CU, 256 on MI355X: dQ blocks are 128 query rows at d = 64, 96 and 256, 256
+# rows at d = 128) and the separate kernels.
 @pytest.mark.parametrize("B,H,N,d,dtype,causal", [
     (1, 64, 512, 64, "f16", True),     # 256 dQ blocks: joint
     (1, 65, 512, 64, "f16", True),     # 260: sequence
@@ -135,6 +135,10 @@ def test_bwd_workload_sampled_heads(name):
     (1, 32, 2048, 128, "bf16", True),  # 256: joint
     (1, 33, 2048, 128, "f16", False),  # 264: sequence
     (1, 3, 4100, 64, "bf16", False),   # 99 (ragged last block): joint
+    (1, 64, 512, 96, "bf16", False),   # 256: joint (three block kinds)
+    (1, 64, 600, 96, "f16", True),     # 320: sequence
+    (1, 32, 1000, 256, "f16", True),   # 256: joint
+    (1, 33, 1000, 256, "bf16", False), # 264: sequence
 ])
 def test_bwd_joint_and_sequence_paths(B, H, N, d, dtype, causal):
     print(f"[fa_bwd] paths B{B} H{H} N{N} d{d} {dtype} causal={causal}", flush=True)
