@@ -15,9 +15,10 @@
 //    run of the unit's 64-key tiles.
 //  * Each wave moves its own K/V tiles HBM -> LDS with buffer_load ... lds
 //    (LDS-DMA: no staging registers, no address VALU) into its own LDS region
-//    (NB = 1 or 2 buffers) of unpadded, XOR-swizzled rows. No other wave
-//    reads that region, so a wave only waits for its own loads (vmcnt); the
-//    workgroup synchronises once, for the merge.
+//    (NB = 1 or 2 buffers) of unpadded, XOR-swizzled rows (d = 64, 128) or of
+//    the main kernel's padded rows (d = 96). No other wave reads that region,
+//    so a wave only waits for its own loads (vmcnt); the workgroup
+//    synchronises once, for the merge.
 //  * The tile step is the main kernel's (scores, online softmax, PV product).
 #pragma once
 #include "fa_fwd_kernel.h"
@@ -37,11 +38,22 @@ __device__ __forceinline__ void wait_vmcnt() {
 // read this wave has issued has returned.
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// LDS of the key-split kernel. d = 64 and 128: unpadded rows whose 16-byte
+// chunks are XOR-swizzled (lds_off<D, 0>). d = 96, whose 12 chunks a row the
+// swizzle does not cover: the main kernel's padded rows (K rows of D+8
+// halves, V rows of fwd_vstr<D>), which the LDS-DMA writes in 1 KB pieces of
+// the padded tile, each padding slot a copy of its row's last chunk.
 template <int D, int NS, int NB>
 struct SplitSmem {
   static constexpr int BC = 64;
-  static constexpr int TILE = BC * D;           // halves per unpadded K or V tile
-  static constexpr int WAVE = 2 * NB * TILE;    // K and V, NB buffers each
+  static constexpr bool PADDED = !(D == 64 || D == 128);
+  static constexpr int KSTR = PADDED ? FwdSmem<D, BC>::KSTR : 0;  // 0: unpadded, swizzled
+  static constexpr int VSTR = PADDED ? FwdSmem<D, BC>::VSTR : 0;
+  static constexpr int KTILE = BC * (PADDED ? KSTR : D);  // halves per K tile
+  static constexpr int VTILE = BC * (PADDED ? VSTR : D);
+  static_assert(KTILE % 512 == 0 && VTILE % 512 == 0, "tiles must be whole 1 KB LDS-DMA pieces");
+  static constexpr int KJ = KTILE / 512, VJ = VTILE / 512;  // pieces per tile
+  static constexpr int WAVE = NB * (KTILE + VTILE);  // K then V, NB buffers each
   static constexpr int HALVES = NS * WAVE;
   // merge area (floats, reusing the tiles): per wave and lane DB*16
   // accumulators, m and the two sums, stored element-major
@@ -97,10 +109,28 @@ __global__ __launch_bounds__(NS * 64) void fa_fwd_split_kernel(const FwdArgs a) 
   const int t_end = min(ntiles, t_begin + tps);
 
   uint16_t* wl = smem + w * SM::WAVE;  // this wave's LDS: K buffers, then V buffers
-  // DMA of tile t into buffer `buf`: chunk slot P = 64 i + lane of the tile
-  // is row P / CPR, slot P % CPR, and receives that row's chunk
-  // (slot ^ swizzle); rows past kv_end lie outside the descriptor and arrive
-  // as zeros
+  auto ktile = [&](int buf) __attribute__((always_inline)) { return wl + buf * SM::KTILE; };
+  auto vtile = [&](int buf) __attribute__((always_inline)) { return wl + NB * SM::KTILE + buf * SM::VTILE; };
+  // padded rows: lane l of piece i carries the chunk at byte 1024 i + 16 l of
+  // the padded tile (row, chunk), a padding slot the row's last chunk; the
+  // per-lane byte offsets are the same for every tile
+  [[maybe_unused]] uint32_t koff[SM::PADDED ? SM::KJ : 1], voff[SM::PADDED ? SM::VJ : 1];
+  if constexpr (SM::PADDED) {
+#pragma unroll
+    for (int i = 0; i < SM::KJ; ++i) {
+      const int o = 1024 * i + 16 * lane, r = o / (2 * SM::KSTR), ch = min(o % (2 * SM::KSTR) / 16, CPR - 1);
+      koff[i] = (uint32_t)(r * (a.k_sr * 2) + ch * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < SM::VJ; ++i) {
+      const int o = 1024 * i + 16 * lane, r = o / (2 * SM::VSTR), ch = min(o % (2 * SM::VSTR) / 16, CPR - 1);
+      voff[i] = (uint32_t)(r * (a.v_sr * 2) + ch * 16);
+    }
+  }
+  // DMA of tile t into buffer `buf`. Unpadded: chunk slot P = 64 i + lane of
+  // the tile is row P / CPR, slot P % CPR, and receives that row's chunk
+  // (slot ^ swizzle). Rows past kv_end lie outside the descriptor and arrive
+  // as zeros.
   auto dma = [&](int t, int buf) __attribute__((always_inline)) {
     const int rows = min(kv_end - t * BC, BC);  // >= 1
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
@@ -109,18 +139,33 @@ __global__ __launch_bounds__(NS * 64) void fa_fwd_split_kernel(const FwdArgs a) 
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(Vg + (int64_t)t * BC * a.v_sr), (short)0, (int)((rows - 1) * (a.v_sr * 2) + D * 2),
         kBufferDword3);
-    uint16_t* kd = wl + buf * SM::TILE;
-    uint16_t* vd = wl + (NB + buf) * SM::TILE;
+    uint16_t* kd = ktile(buf);
+    uint16_t* vd = vtile(buf);
+    if constexpr (SM::PADDED) {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int P = 64 * i + lane;
-      const int r = P / CPR, ch = (P % CPR) ^ lds_swz<D>(r);
-      const uint32_t ko = (uint32_t)(r * (a.k_sr * 2) + ch * 16);
-      const uint32_t vo = (uint32_t)(r * (a.v_sr * 2) + ch * 16);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kd + 64 * i * 8),
-                                               16, ko, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vd + 64 * i * 8),
-                                               16, vo, 0, 0, 0);
+      for (int i = 0; i < SM::KJ; ++i) {
+        const uint32_t o = koff[i];  // the builtin given koff[i] itself loses the host-side kernel stub
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kd + 512 * i), 16,
+                                                 o, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < SM::VJ; ++i) {
+        const uint32_t o = voff[i];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vd + 512 * i), 16,
+                                                 o, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int P = 64 * i + lane;
+        const int r = P / CPR, ch = (P % CPR) ^ lds_swz<D>(r);
+        const uint32_t ko = (uint32_t)(r * (a.k_sr * 2) + ch * 16);
+        const uint32_t vo = (uint32_t)(r * (a.v_sr * 2) + ch * 16);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kd + 64 * i * 8),
+                                                 16, ko, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vd + 64 * i * 8),
+                                                 16, vo, 0, 0, 0);
+      }
     }
   };
 
@@ -148,15 +193,15 @@ __global__ __launch_bounds__(NS * 64) void fa_fwd_split_kernel(const FwdArgs a) 
       const int buf = NB == 2 ? (t - t_begin) & 1 : 0;
       if (NB == 2 && t + 1 < t_end) {
         dma(t + 1, buf ^ 1);
-        wait_vmcnt<2 * LOADS>();  // tile t has landed; tile t+1 may be in flight
+        wait_vmcnt<SM::PADDED ? SM::KJ + SM::VJ : 2 * LOADS>();  // tile t has landed; tile t+1 may be in flight
       } else {
         wait_vmcnt<0>();
       }
       const int key0 = t * BC;
       const bool need_mask = (key0 + BC > Nb) || (CAUSAL && key0 + BC - 1 > qw0);
-      tile_step_fwd<D, DT, CAUSAL, 1, BC, 0, 0, PF>(t == t_begin, need_mask, wl + buf * SM::TILE,
-                                                    wl + (NB + buf) * SM::TILE, key0, Nb, qw0, lane, a.c, qf,
-                                                    oacc, m_run, l_run);
+      tile_step_fwd<D, DT, CAUSAL, 1, BC, SM::KSTR, SM::VSTR, PF>(t == t_begin, need_mask, ktile(buf), vtile(buf),
+                                                                  key0, Nb, qw0, lane, a.c, qf, oacc, m_run,
+                                                                  l_run);
       // one buffer: the next tile's DMA writes the buffer this tile has just
       // read, so it waits until those LDS reads have returned (lgkmcnt 0),
       // and the fences keep the compiler from moving the reads below the wait or
