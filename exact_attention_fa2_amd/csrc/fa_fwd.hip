@@ -39,9 +39,9 @@ int pick(FwdArgs a, hipStream_t st) {
     constexpr int64_t kSplitMax = D == 64 ? 512 : 256;
     if (units <= kSplitMax) return launch_fwd_split(a, D, DT, CAUSAL, 4, st);
   }
-  if constexpr (D == 96) {
-    // key split over 4 waves, padded rows by LDS-DMA (100 KB of LDS: one
-    // workgroup per CU), while every unit's workgroup fits the chip at once
+  if constexpr (D == 96 || D == 256) {
+    // key split over 4 waves, padded rows by LDS-DMA (100 / 140 KB of LDS:
+    // one workgroup per CU), while every unit's workgroup fits the chip at once
     if ((int64_t)a.B * a.H * ((a.N + 31) / 32) <= 256) return launch_fwd_split(a, D, DT, CAUSAL, 4, st);
   }
   if constexpr (D == 64 || D == 128) {

@@ -35,6 +35,7 @@ int launch_fwd_split(FwdArgs a, int d, int dt, bool causal, int ns, hipStream_t 
     case 64: return split_dt<64>(a, dt, causal, ns, st);
     case 96: return split_dt<96>(a, dt, causal, ns, st);
     case 128: return split_dt<128>(a, dt, causal, ns, st);
+    case 256: return split_dt<256>(a, dt, causal, ns, st);
     default: return FA_ERR_UNSUPPORTED;
   }
 }

@@ -39,20 +39,22 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // LDS of the key-split kernel. d = 64 and 128: unpadded rows whose 16-byte
-// chunks are XOR-swizzled (lds_off<D, 0>). d = 96, whose 12 chunks a row the
+// chunks are XOR-swizzled (lds_off<D, 0>). d = 96 and 256, whose rows the
 // swizzle does not cover: the main kernel's padded rows (K rows of D+8
-// halves, V rows of fwd_vstr<D>), which the LDS-DMA writes in 1 KB pieces of
-// the padded tile, each padding slot a copy of its row's last chunk.
+// halves, V rows of fwd_vstr<D>; 32-key tiles at d = 256, as in the main
+// kernel), which the LDS-DMA writes in 1 KB pieces of the padded tile, each
+// padding slot a copy of its row's last chunk. A tile region is rounded up
+// to whole pieces; the lanes past the tile's last row load rows outside the
+// buffer descriptor, which arrive as zeros.
 template <int D, int NS, int NB>
 struct SplitSmem {
-  static constexpr int BC = 64;
+  static constexpr int BC = D == 256 ? 32 : 64;
   static constexpr bool PADDED = !(D == 64 || D == 128);
   static constexpr int KSTR = PADDED ? FwdSmem<D, BC>::KSTR : 0;  // 0: unpadded, swizzled
   static constexpr int VSTR = PADDED ? FwdSmem<D, BC>::VSTR : 0;
-  static constexpr int KTILE = BC * (PADDED ? KSTR : D);  // halves per K tile
-  static constexpr int VTILE = BC * (PADDED ? VSTR : D);
-  static_assert(KTILE % 512 == 0 && VTILE % 512 == 0, "tiles must be whole 1 KB LDS-DMA pieces");
-  static constexpr int KJ = KTILE / 512, VJ = VTILE / 512;  // pieces per tile
+  static constexpr int KTILE = (BC * (PADDED ? KSTR : D) + 511) / 512 * 512;  // halves per K tile region
+  static constexpr int VTILE = (BC * (PADDED ? VSTR : D) + 511) / 512 * 512;
+  static constexpr int KJ = KTILE / 512, VJ = VTILE / 512;  // 1 KB pieces per tile
   static constexpr int WAVE = NB * (KTILE + VTILE);  // K then V, NB buffers each
   static constexpr int HALVES = NS * WAVE;
   // merge area (floats, reusing the tiles): per wave and lane DB*16
@@ -63,9 +65,9 @@ struct SplitSmem {
 
 template <int D, int DT, bool CAUSAL, int NS, int NB, int PF>
 __global__ __launch_bounds__(NS * 64) void fa_fwd_split_kernel(const FwdArgs a) {
-  constexpr int BC = 64, KK = D / 16, DB = D / 32, CPR = D / 8;
-  constexpr int LOADS = BC * CPR / 64;  // DMA loads per wave per tensor per tile
   using SM = SplitSmem<D, NS, NB>;
+  constexpr int BC = SM::BC, KK = D / 16, DB = D / 32, CPR = D / 8;
+  constexpr int LOADS = BC * CPR / 64;  // DMA loads per wave per tensor per tile (unpadded rows)
   __shared__ __attribute__((aligned(16))) uint16_t smem[SM::HALVES];
 
   // ---- workgroup -> (batch, head, unit), XCD-aware as in fa_fwd_kernel ----
@@ -259,8 +261,13 @@ __global__ __launch_bounds__(NS * 64) void fa_fwd_split_kernel(const FwdArgs a) 
   // of the partials, which the same wave's LDS ops complete in order) and
   // writes whole 16-byte row chunks
   constexpr int OSTR = D + 8;
-  uint16_t* ob = smem + NS * SM::PART * 64 * 2;  // past the partials
-  static_assert(NS * SM::PART * 64 * 2 + 32 * OSTR <= SM::HALVES, "output staging must fit");
+  // past the partials where they leave room; else (d = 256) over the slots of
+  // waves 1.. (slot 0 is unused), whose partials wave 0 has consumed: every
+  // store below depends on the merged values
+  constexpr bool OB_PAST = NS * SM::PART * 64 * 2 + 32 * OSTR <= SM::HALVES;
+  uint16_t* ob = smem + (OB_PAST ? NS : 1) * SM::PART * 64 * 2;
+  static_assert(SM::PART * 64 * 2 + 32 * OSTR <= SM::HALVES, "output staging must fit");
+  if constexpr (!OB_PAST) wave_lds_sync();
   const float l_tot = l_run[0][0] + xor_lane32(l_run[0][0]);
   const float l_lse = DT == DT_F16 ? l_tot : l_run[1][0] + xor_lane32(l_run[1][0]);
   const float inv = 1.f / l_tot;

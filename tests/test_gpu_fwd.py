@@ -87,7 +87,7 @@ def test_workload_parity(name, seed):
 
 # The dispatch runs the key-split kernel (one workgroup per 32-row unit, keys
 # split over 4 waves) while B*H*ceil(N/32) is at most 512 (d=64) or 256
-# (d=96, padded rows; d=128), and the main kernel past that; at d=64 it splits
+# (d=96 and 256, padded rows; d=128), and the main kernel past that; at d=64 it splits
 # over 8 waves while that count is at most 256 and N >= 1024. Both sides of each boundary,
 # against the oracle; long rows split over the waves with large logits
 # (rescales in the merge), and short sequences that leave waves without keys.
@@ -100,7 +100,9 @@ def test_workload_parity(name, seed):
     (1, 1024, 64, "bf16", True), (1, 8192, 64, "f16", False),
     (4, 400, 64, "f16", False), (2, 1000, 64, "bf16", True), (8, 1000, 64, "f16", False),
     (8, 1024, 96, "f16", False), (8, 1025, 96, "bf16", True), (1, 5000, 96, "bf16", False),
-    (3, 100, 96, "f16", True), (2, 2100, 96, "f16", True)])
+    (3, 100, 96, "f16", True), (2, 2100, 96, "f16", True),
+    (4, 1024, 256, "bf16", False), (8, 1024, 256, "f16", True), (1, 6400, 256, "f16", False),
+    (9, 1000, 256, "bf16", False), (2, 100, 256, "bf16", True)])
 def test_key_split_path(H, N, d, dtype, causal):
     rows = P.sample_rows(1, H, N, 300, H + N) if H * N * N > 4 * 1024 * 1024 else None
     run_case(1, H, N, d, dtype, causal, 40 + H, None, 2.5, 1.0, rows)
