@@ -464,6 +464,27 @@ def test_strided_layouts_on_short_map_kernels(B, N, H, dtype, causal):
     assert torch.equal(o2.cpu(), o.cpu()) and torch.equal(lse2.cpu(), lse.cpu())
 
 
+@pytest.mark.parametrize("d,dtype,causal", [(96, "f16", False), (96, "bf16", True), (256, "bf16", False),
+                                            (256, "f16", True)])
+def test_strided_layouts_on_padded_key_split(d, dtype, causal):
+    # the key-split kernel's padded-row LDS-DMA at d = 96 and 256 reads K and
+    # V through the row stride of [B, N, H, d] views and of packed QKV
+    B, N, H = 1, 1000, 2
+    say(f"[fa_fwd_strided] padded key split B{B} N{N} H{H} d{d} {dtype} causal={causal}")
+    q, k, v = inputs.make_qkv(B, N, H, d, dtype, 170 + d)  # drawn directly in [B, N, H, d]
+    o, lse = fa.attention_bnhd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal)
+    torch.cuda.synchronize()
+    perm = lambda t: P.decode(t, dtype).transpose(0, 2, 1, 3)
+    qd, kd, vd = perm(q), perm(k), perm(v)
+    ro, rl = oracle.attention_fwd(qd, kd, vd, d ** -0.5, causal)
+    P.gate_o(P.to64(o).transpose(0, 2, 1, 3), ro, dtype)
+    P.gate_lse(P.to64(lse), rl)
+    qkv = torch.stack([q, k, v], dim=2).contiguous()  # [B, N, 3, H, d]
+    o2, lse2 = fa.attention_qkvpacked(qkv.to(DEV), causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.cpu(), o.cpu()) and torch.equal(lse2.cpu(), lse.cpu())
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_packed_qkv_pages_shape(d):
     # an 80x80 map with C = 256 channels split into heads of d
