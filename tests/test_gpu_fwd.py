@@ -505,6 +505,29 @@ def test_packed_qkv_pages_shape(d):
 # ---------------------------------------------------------------------------
 # variable-length packed batches
 # ---------------------------------------------------------------------------
+@pytest.mark.parametrize("d,dtype", [(96, "f16"), (256, "bf16")])
+def test_varlen_padded_key_split(d, dtype):
+    # few sequences at d = 96 and 256: the key-split kernel's padded-row path
+    # with the rows of each sequence found through cu_seqlens
+    seqlens, H = [400, 1, 0, 100, 1000], 1
+    say(f"[fa_fwd_varlen] {seqlens} H={H} d={d} {dtype} causal=False/True")
+    q, k, v, cu = inputs.make_varlen(seqlens, H, d, dtype, 83)
+    qd, kd, vd = (P.decode(x, dtype) for x in (q, k, v))
+    for causal in (False, True):
+        o, lse = fa.attention_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), max(seqlens), causal=causal)
+        torch.cuda.synchronize()
+        og, lg = P.to64(o), P.to64(lse)
+        for b, n in enumerate(seqlens):
+            if n == 0:
+                continue
+            s0 = int(cu[b])
+            sl = slice(s0, s0 + n)
+            t = lambda x: x[sl].transpose(1, 0, 2)[None]
+            ro, rl = oracle.attention_fwd(t(qd), t(kd), t(vd), d ** -0.5, causal)
+            P.gate_o(og[sl].transpose(1, 0, 2)[None], ro, dtype, what=f"O seq {b}")
+            P.gate_lse(lg[:, sl][None], rl)
+
+
 @pytest.mark.parametrize("seqlens,H", [([400, 0, 37, 129], 2), ([1100, 0, 37, 2000], 1)])
 def test_varlen_small_grid(seqlens, H):
     # few sequences: the key-split kernel's varlen path (4 waves per unit;
