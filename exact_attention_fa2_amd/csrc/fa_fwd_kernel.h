@@ -42,6 +42,8 @@
 //  * A head's 32-row units are spread evenly over its blocks, one unit per
 //    wave; waves without a unit only help with the K/V loads.
 #pragma once
+#include <type_traits>
+
 #include "fa_device.h"
 
 namespace fa {
@@ -324,17 +326,28 @@ __device__ __forceinline__ void tile_step_fwd(bool first, bool masked, const uin
   }
 }
 
-// Workgroups per CU the compiler is to fit. The 4-wave d=96 kernel left to
-// itself takes 276-280 VGPRs (one wave per SIMD); held to two workgroups it
-// fits 184-191 without spills (B4 H16 N4096 fp16: 454 vs 459 us). Three
-// spill; the 4-wave d=128 kernel gains nothing from two.
+// Waves per SIMD the compiler is to fit (the second launch bound). The
+// 4-wave d=96 kernel left to itself takes 276-280 VGPRs (one wave per SIMD);
+// held to two it fits 184-191 without spills (B4 H16 N4096 fp16: 454 vs
+// 459 us); three spill.
 template <int D, int NW>
-constexpr int fwd_min_blocks() {
+constexpr int fwd_min_waves() {
   return D == 96 && NW == 4 ? 2 : 1;
 }
 
+// Whether the main tile loop runs in pairs of tiles, so that the LDS stage
+// is a constant in each copy of the tile step. Two kernels keep the
+// single-tile loop, because in pairs they lose occupancy or spill: the 4-wave
+// d=128 kernels (fp16 causal: more than 256 VGPRs) and the 8-wave d=64 fp16
+// causal kernel (131 VGPRs, 3 waves per SIMD instead of 4; held to 128 it
+// spills).
+template <int D, int DT, bool CAUSAL, int NW>
+constexpr bool fwd_pair_loop() {
+  return !(D == 128 && NW == 4) && !(D == 64 && DT == DT_F16 && CAUSAL && NW == 8);
+}
+
 template <int D, int DT, bool CAUSAL, int NW, int QB, int BC, int PF, bool LS = false>
-__global__ __launch_bounds__(NW * 64, (fwd_min_blocks<D, NW>())) void fa_fwd_kernel(const FwdArgs a) {
+__global__ __launch_bounds__(NW * 64, (fwd_min_waves<D, NW>())) void fa_fwd_kernel(const FwdArgs a) {
   static_assert(QB == 1, "one 32-row unit per wave");
   constexpr int NT = NW * 64;
   constexpr int QW = 32 * QB;          // query rows per wave
@@ -452,7 +465,7 @@ __global__ __launch_bounds__(NW * 64, (fwd_min_blocks<D, NW>())) void fa_fwd_ker
       vst[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff[c], 0, 0));
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](int buf) __attribute__((always_inline)) {
     uint16_t* sk = smem + buf * SM::STAGE;
     uint16_t* sv = sk + SM::KTILE;
 #pragma unroll
@@ -499,18 +512,34 @@ __global__ __launch_bounds__(NW * 64, (fwd_min_blocks<D, NW>())) void fa_fwd_ker
     const int wnt = (wave_end + BC - 1) / BC;
     const bool tail32 = BC == 64 && wave_end - (wnt - 1) * BC <= 32;
     const int nmain = tail32 ? wnt - 1 : wnt;
-    int t = 0;
-    for (; t < nmain; ++t) {
+    // tile t computes from LDS stage P = t % 2; taken in pairs from t = 0,
+    // P is a constant in each copy of the step and the stage's LDS addresses
+    // are immediate offsets from fixed bases
+    auto main_step = [&](int t, auto stage) __attribute__((always_inline)) {
+      const int P = stage;
       __syncthreads();
       if (t + 1 < ntiles) fetch(t + 1);
       const int key0 = t * BC;
-      const uint16_t* sk = smem + (t & 1) * SM::STAGE;
+      const uint16_t* sk = smem + P * SM::STAGE;
       const uint16_t* sv = sk + SM::KTILE;
       // ragged last tile, or (causal) keys after some query of this wave
       const bool need_mask = (key0 + BC > Nb) || (CAUSAL && key0 + BC - 1 > qw0);
-      tile_step_fwd<D, DT, CAUSAL, QB, BC, SM::KSTR, SM::VSTR, PF, LS>(t == 0, need_mask, sk, sv, key0, Nb, qw0,
-                                                               lane, a.c, qf, oacc, m_run, l_run);
-      if (t + 1 < ntiles) stash((t + 1) & 1);
+      tile_step_fwd<D, DT, CAUSAL, QB, BC, SM::KSTR, SM::VSTR, PF, LS>(P == 0 && t == 0, need_mask, sk, sv, key0, Nb,
+                                                               qw0, lane, a.c, qf, oacc, m_run, l_run);
+      if (t + 1 < ntiles) stash(P ^ 1);
+    };
+    int t = 0;
+    if constexpr (fwd_pair_loop<D, DT, CAUSAL, NW>()) {
+      for (; t + 1 < nmain; t += 2) {
+        main_step(t, std::integral_constant<int, 0>{});
+        main_step(t + 1, std::integral_constant<int, 1>{});
+      }
+      if (t < nmain) {
+        main_step(t, std::integral_constant<int, 0>{});
+        ++t;
+      }
+    } else {
+      for (; t < nmain; ++t) main_step(t, t & 1);
     }
     if constexpr (BC == 64) {
       if (tail32) {
